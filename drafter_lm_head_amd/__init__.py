@@ -1,0 +1,250 @@
+"""Python binding of libvocabtrim, the gfx950 frequency-ranked drafter head.
+
+Argument marshalling only: every step runs in the HIP library declared in
+``include/vocabtrim.h``. torch supplies device memory and the current
+stream. The functions keep the C names:
+
+* ``vt_count_freq(ids, V)``            -> (counts uint32[V], n_invalid)
+* ``vt_select_vocab(counts, V_high)``  -> (t2f, f2t, sel_sum, tot_sum)
+* ``vt_gather_head(W, t2f)``           -> W_trim
+* ``vt_draft_head(h, W_trim, t2f, k)`` -> (full_ids int32[M, k], probs f32[M, k])
+* ``vt_head_logits(h, W_trim)``        -> logits f32[M, V_high] (checks only)
+
+bfloat16 arrays may be passed as ``torch.bfloat16`` or as their 16-bit
+patterns (``torch.int16`` / ``torch.uint16``). Results stay on the device;
+nothing here synchronises with the host. If the library is missing the
+calls raise: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "VtError", "lib", "lib_path", "VT_K_MAX", "VT_M_MAX", "VT_D_MAX",
+    "VT_VHIGH_MAX", "vt_count_freq", "vt_select_vocab", "vt_gather_head",
+    "vt_draft_head", "vt_head_logits", "vt_count_freq_workspace_size",
+    "vt_select_vocab_workspace_size", "vt_draft_head_workspace_size",
+    "coverage",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libvocabtrim.so")
+
+VT_OK, VT_ERR_INVALID_ARG, VT_ERR_UNSUPPORTED, VT_ERR_WORKSPACE, VT_ERR_HIP = 0, -1, -2, -3, -4
+VT_K_MAX, VT_M_MAX, VT_D_MAX, VT_VHIGH_MAX = 64, 64, 8192, 262144
+
+_lock = threading.Lock()
+_lib = None
+
+_P, _I32, _U64, _SZ, _INT = C.c_void_p, C.c_int32, C.c_uint64, C.c_size_t, C.c_int
+_SIGS = {
+    "vt_status_string": (C.c_char_p, [_INT]),
+    "vt_version": (_INT, []),
+    "vt_count_freq_workspace_size": (_SZ, [_U64, _I32]),
+    "vt_count_freq": (_INT, [_P, _U64, _I32, _P, _INT, _P, _P, _SZ, _P]),
+    "vt_select_vocab_workspace_size": (_SZ, [_I32, _I32]),
+    "vt_select_vocab": (_INT, [_P, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
+    "vt_gather_head": (_INT, [_P, _I32, _I32, _P, _I32, _P, _P, _P]),
+    "vt_draft_head_workspace_size": (_SZ, [_I32, _I32, _I32, _I32]),
+    "vt_draft_head": (_INT, [_P, _I32, _I32, _P, _I32, _P, _I32, _P, _P, _P, _SZ, _P]),
+    "vt_head_logits": (_INT, [_P, _I32, _I32, _P, _I32, _P, _P]),
+}
+
+
+class VtError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {lib().vt_status_string(status).decode()} (status {status})")
+
+
+def lib():
+    """The loaded library (ctypes handle). Raises if it was not built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(lib_path):
+                raise RuntimeError(
+                    f"{lib_path} is missing: build it with __graft_entry__.build() "
+                    "(hipcc, gfx950); there is no fallback implementation")
+            h = C.CDLL(lib_path)
+            for name, (res, args) in _SIGS.items():
+                f = getattr(h, name)
+                f.restype, f.argtypes = res, args
+            _lib = h
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != VT_OK:
+        raise VtError(status, what)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtypes, ndim: int | None = None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-d, got shape {tuple(t.shape)}")
+    return t
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+# One cached workspace per (device, kind); grown on demand. The draft-head
+# workspace is zero-filled when allocated, as the C ABI requires.
+_ws_cache: dict = {}
+
+
+def _workspace(device: torch.device, kind: str, nbytes: int, zero: bool) -> torch.Tensor:
+    key = (device.index, kind)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        n = max(nbytes, 256)
+        ws = (torch.zeros if zero else torch.empty)(n, dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def vt_count_freq_workspace_size(n: int, V: int) -> int:
+    return int(lib().vt_count_freq_workspace_size(n, V))
+
+
+def vt_select_vocab_workspace_size(V: int, V_high: int) -> int:
+    return int(lib().vt_select_vocab_workspace_size(V, V_high))
+
+
+def vt_draft_head_workspace_size(M: int, V_high: int, d: int, k: int) -> int:
+    return int(lib().vt_draft_head_workspace_size(M, V_high, d, k))
+
+
+def vt_count_freq(ids: torch.Tensor, V: int, counts: torch.Tensor | None = None,
+                  n_invalid: torch.Tensor | None = None, accumulate: bool = False,
+                  ws: torch.Tensor | None = None):
+    """Histogram of token ids (VocabTrim Step 1). Returns (counts, n_invalid)."""
+    _dev(ids, "ids", (torch.int32,), 1)
+    dev = ids.device
+    if counts is None:
+        if accumulate:
+            raise ValueError("accumulate needs existing counts")
+        counts = torch.empty(V, dtype=torch.int32, device=dev).view(torch.uint32)
+    if n_invalid is None:
+        if accumulate:
+            raise ValueError("accumulate needs an existing n_invalid")
+        n_invalid = torch.empty(1, dtype=torch.int64, device=dev).view(torch.uint64)
+    _dev(counts, "counts", (torch.uint32, torch.int32), 1)
+    _dev(n_invalid, "n_invalid", (torch.uint64, torch.int64), 1)
+    n = ids.numel()
+    need = vt_count_freq_workspace_size(n, V)
+    ws = ws if ws is not None else _workspace(dev, "count", need, False)
+    _check(lib().vt_count_freq(_ptr(ids) if n else None, n, V, _ptr(counts), int(bool(accumulate)),
+                               _ptr(n_invalid), _ptr(ws), ws.numel(), _stream(ids)),
+           "vt_count_freq")
+    return counts, n_invalid
+
+
+def vt_select_vocab(counts: torch.Tensor, V_high: int, want_f2t: bool = True,
+                    ws: torch.Tensor | None = None):
+    """Top-V_high ids by (count desc, id asc) (VocabTrim Step 2).
+
+    Returns device tensors (t2f int32[V_high], f2t int32[V] or None,
+    sel_sum uint64[1], tot_sum uint64[1]).
+    """
+    _dev(counts, "counts", (torch.uint32, torch.int32), 1)
+    dev = counts.device
+    V = counts.numel()
+    t2f = torch.empty(V_high, dtype=torch.int32, device=dev)
+    f2t = torch.empty(V, dtype=torch.int32, device=dev) if want_f2t else None
+    sums = torch.empty(2, dtype=torch.int64, device=dev).view(torch.uint64)
+    need = vt_select_vocab_workspace_size(V, V_high)
+    ws = ws if ws is not None else _workspace(dev, "select", need, False)
+    _check(lib().vt_select_vocab(_ptr(counts), V, V_high, _ptr(t2f), _ptr(f2t),
+                                 _ptr(sums[0:1]), _ptr(sums[1:2]), _ptr(ws), ws.numel(),
+                                 _stream(counts)), "vt_select_vocab")
+    return t2f, f2t, sums[0:1], sums[1:2]
+
+
+def coverage(sel_sum: torch.Tensor, tot_sum: torch.Tensor) -> float:
+    """sel / tot on the host (synchronises); NaN when nothing was counted."""
+    s = int(sel_sum.view(torch.int64).item())
+    t = int(tot_sum.view(torch.int64).item())
+    return float("nan") if t == 0 else s / t
+
+
+def vt_gather_head(W: torch.Tensor, t2f: torch.Tensor, out: torch.Tensor | None = None,
+                   n_bad: torch.Tensor | None = None) -> torch.Tensor:
+    """W_trim = W[t2f] (VocabTrim Step 3)."""
+    _dev(W, "W", _BF16, 2)
+    _dev(t2f, "t2f", (torch.int32,), 1)
+    V, d = W.shape
+    V_high = t2f.numel()
+    if out is None:
+        out = torch.empty((V_high, d), dtype=W.dtype, device=W.device)
+    _dev(out, "out", _BF16, 2)
+    if tuple(out.shape) != (V_high, d):
+        raise ValueError("out must be [V_high, d]")
+    if n_bad is not None:
+        _dev(n_bad, "n_bad", (torch.int32, torch.uint32), 1)
+    _check(lib().vt_gather_head(_ptr(W), V, d, _ptr(t2f), V_high, _ptr(out), _ptr(n_bad),
+                                _stream(W)), "vt_gather_head")
+    return out
+
+
+def vt_draft_head(h: torch.Tensor, W_trim: torch.Tensor, t2f: torch.Tensor, k: int,
+                  full_ids: torch.Tensor | None = None, probs: torch.Tensor | None = None,
+                  ws: torch.Tensor | None = None):
+    """One draft step (VocabTrim Step 4): (full_ids[M, k], probs[M, k])."""
+    _dev(h, "h", _BF16, 2)
+    _dev(W_trim, "W_trim", _BF16, 2)
+    _dev(t2f, "t2f", (torch.int32,), 1)
+    M, d = h.shape
+    V_high = W_trim.shape[0]
+    if W_trim.shape[1] != d or t2f.numel() != V_high:
+        raise ValueError("shape mismatch between h, W_trim and t2f")
+    dev = h.device
+    if full_ids is None:
+        full_ids = torch.empty((M, k), dtype=torch.int32, device=dev)
+    if probs is None:
+        probs = torch.empty((M, k), dtype=torch.float32, device=dev)
+    _dev(full_ids, "full_ids", (torch.int32,))
+    _dev(probs, "probs", (torch.float32,))
+    if full_ids.numel() != M * k or probs.numel() != M * k:
+        raise ValueError("outputs must hold M * k entries")
+    if ws is None:
+        need = vt_draft_head_workspace_size(M, V_high, d, k)
+        ws = _workspace(dev, "head", need, True)
+    _check(lib().vt_draft_head(_ptr(h), M, d, _ptr(W_trim), V_high, _ptr(t2f), k,
+                               _ptr(full_ids), _ptr(probs), _ptr(ws), ws.numel(), _stream(h)),
+           "vt_draft_head")
+    return full_ids, probs
+
+
+def vt_head_logits(h: torch.Tensor, W_trim: torch.Tensor,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """fp32 trimmed logits [M, V_high] (parity diagnostics)."""
+    _dev(h, "h", _BF16, 2)
+    _dev(W_trim, "W_trim", _BF16, 2)
+    M, d = h.shape
+    V_high = W_trim.shape[0]
+    if W_trim.shape[1] != d:
+        raise ValueError("shape mismatch between h and W_trim")
+    if out is None:
+        out = torch.empty((M, V_high), dtype=torch.float32, device=h.device)
+    _dev(out, "out", (torch.float32,))
+    _check(lib().vt_head_logits(_ptr(h), M, d, _ptr(W_trim), V_high, _ptr(out), _stream(h)),
+           "vt_head_logits")
+    return out

@@ -1,0 +1,144 @@
+// C ABI of the frequency-ranked drafter head (declared in vocabtrim.h):
+// argument validation before any HIP call, workspace sizing, and dispatch
+// to the kernels on the caller's stream.
+#include "vocabtrim.h"
+
+#include <stdint.h>
+
+#include "vt_internal.hpp"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) {
+  return ((uintptr_t)p & (a - 1)) == 0;
+}
+
+bool valid_d(int32_t d) { return d >= 8 && d <= VT_D_MAX && d % 8 == 0; }
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return VT_OK;
+  (void)hipGetLastError();
+  return VT_ERR_HIP;
+}
+
+hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *vt_status_string(int status) {
+  switch (status) {
+    case VT_OK: return "ok";
+    case VT_ERR_INVALID_ARG: return "invalid argument";
+    case VT_ERR_UNSUPPORTED: return "unsupported size for this build";
+    case VT_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case VT_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int vt_version(void) { return VT_ABI_VERSION; }
+
+// ------------------------------------------------------------------ count
+size_t vt_count_freq_workspace_size(uint64_t n, int32_t V) {
+  if (V <= 0) return 0;
+  const vt::CountPlan p = vt::count_plan(n, V);
+  return p.partial_bytes + p.inv_bytes;
+}
+
+int vt_count_freq(const int32_t *ids, uint64_t n, int32_t V, uint32_t *counts,
+                  int accumulate, uint64_t *n_invalid, void *ws,
+                  size_t ws_bytes, void *stream) {
+  if (V <= 0 || n > UINT32_MAX || !counts || !n_invalid) return VT_ERR_INVALID_ARG;
+  if (n > 0 && (!ids || !aligned(ids, 16))) return VT_ERR_INVALID_ARG;
+  if (!ws || !aligned(ws, 256) || ws_bytes < vt_count_freq_workspace_size(n, V))
+    return VT_ERR_WORKSPACE;
+  return hip_status(vt::launch_count(ids, n, V, counts, accumulate ? 1 : 0,
+                                     n_invalid, ws, as_stream(stream)));
+}
+
+// ----------------------------------------------------------------- select
+size_t vt_select_vocab_workspace_size(int32_t V, int32_t V_high) {
+  if (V <= 0 || V_high <= 0 || V_high > V) return 0;
+  return vt::select_ws_bytes(V, V_high);
+}
+
+int vt_select_vocab(const uint32_t *counts, int32_t V, int32_t V_high,
+                    int32_t *t2f, int32_t *f2t, uint64_t *sel_sum,
+                    uint64_t *tot_sum, void *ws, size_t ws_bytes,
+                    void *stream) {
+  if (!counts || !t2f || !sel_sum || !tot_sum) return VT_ERR_INVALID_ARG;
+  if (V <= 0 || V_high <= 0 || V_high > V) return VT_ERR_INVALID_ARG;
+  if (!ws || !aligned(ws, 256) ||
+      ws_bytes < vt_select_vocab_workspace_size(V, V_high))
+    return VT_ERR_WORKSPACE;
+  return hip_status(vt::launch_select(counts, V, V_high, t2f, f2t, sel_sum,
+                                      tot_sum, ws, as_stream(stream)));
+}
+
+// ----------------------------------------------------------------- gather
+int vt_gather_head(const uint16_t *W, int32_t V, int32_t d,
+                   const int32_t *t2f, int32_t V_high, uint16_t *W_trim,
+                   uint32_t *n_bad, void *stream) {
+  if (!W || !t2f || !W_trim) return VT_ERR_INVALID_ARG;
+  if (V <= 0 || V_high <= 0 || !valid_d(d)) return VT_ERR_INVALID_ARG;
+  if (!aligned(W, 16) || !aligned(W_trim, 16)) return VT_ERR_INVALID_ARG;
+  if (overlaps(W, (size_t)V * d * 2, W_trim, (size_t)V_high * d * 2))
+    return VT_ERR_INVALID_ARG;
+  return hip_status(vt::launch_gather(W, V, d, t2f, V_high, W_trim, n_bad,
+                                      as_stream(stream)));
+}
+
+// ------------------------------------------------------------- draft head
+static int check_head(const uint16_t *h, int32_t M, int32_t d,
+                      const uint16_t *W_trim, int32_t V_high) {
+  if (!h || !W_trim) return VT_ERR_INVALID_ARG;
+  if (M <= 0 || V_high <= 0 || !valid_d(d)) return VT_ERR_INVALID_ARG;
+  if (!aligned(h, 16) || !aligned(W_trim, 16)) return VT_ERR_INVALID_ARG;
+  if (M > VT_M_MAX || V_high > VT_VHIGH_MAX) return VT_ERR_UNSUPPORTED;
+  return VT_OK;
+}
+
+size_t vt_draft_head_workspace_size(int32_t M, int32_t V_high, int32_t d,
+                                    int32_t k) {
+  (void)d;
+  if (M <= 0 || M > VT_M_MAX || V_high <= 0 || V_high > VT_VHIGH_MAX ||
+      k <= 0 || k > VT_K_MAX)
+    return 0;
+  return vt::head_plan(M, V_high, k).bytes;
+}
+
+int vt_draft_head(const uint16_t *h, int32_t M, int32_t d,
+                  const uint16_t *W_trim, int32_t V_high, const int32_t *t2f,
+                  int32_t k, int32_t *full_ids, float *probs, void *ws,
+                  size_t ws_bytes, void *stream) {
+  int st = check_head(h, M, d, W_trim, V_high);
+  if (st != VT_OK) return st;
+  if (!t2f || !full_ids || !probs) return VT_ERR_INVALID_ARG;
+  if (k <= 0 || k > V_high) return VT_ERR_INVALID_ARG;
+  if (k > VT_K_MAX) return VT_ERR_UNSUPPORTED;
+  if (!ws || !aligned(ws, 256) ||
+      ws_bytes < vt_draft_head_workspace_size(M, V_high, d, k))
+    return VT_ERR_WORKSPACE;
+  return hip_status(vt::launch_draft_head(h, M, d, W_trim, V_high, t2f, k,
+                                          full_ids, probs, ws,
+                                          as_stream(stream)));
+}
+
+int vt_head_logits(const uint16_t *h, int32_t M, int32_t d,
+                   const uint16_t *W_trim, int32_t V_high, float *logits,
+                   void *stream) {
+  int st = check_head(h, M, d, W_trim, V_high);
+  if (st != VT_OK) return st;
+  if (!logits) return VT_ERR_INVALID_ARG;
+  return hip_status(
+      vt::launch_head_logits(h, M, d, W_trim, V_high, logits, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,165 @@
+// Token-id histogram (VocabTrim page, Implementation, Step 1; FR-Spec notes,
+// key design: token frequencies over a corpus), for gfx950.
+//
+// The bins of a large vocabulary (128k-152k ids) do not fit one CU's LDS, so
+// the id range is cut into R ranges of at most kRangeBins bins and every
+// (range, chunk-of-ids) pair is one workgroup that counts into LDS with LDS
+// atomics. The R workgroups of one chunk read the same ids; they are placed
+// on the same XCD and dispatched back to back, so the repeated reads are
+// served by that XCD's L2 and the Infinity Cache rather than HBM. Each
+// workgroup then stores its range of counts to its own row of a partial
+// table (no global atomics), and a second kernel sums the rows, which keeps
+// the result independent of scheduling.
+#include "vt_internal.hpp"
+
+namespace vt {
+
+namespace {
+
+constexpr int kCountThreads = 1024;
+
+__device__ __forceinline__ void count_one(int32_t id, uint32_t lo, uint32_t nb,
+                                          uint32_t *s_bins) {
+  const uint32_t b = (uint32_t)id - lo;  // wraps for ids below the range
+  if (b < nb) atomicAdd(&s_bins[b], 1u);
+}
+
+__global__ __launch_bounds__(kCountThreads) void count_partial_kernel(
+    const int32_t *__restrict__ ids, uint64_t n, int32_t V, int32_t range_bins,
+    int32_t n_ranges, int32_t n_chunks, uint64_t chunk_len,
+    uint32_t *__restrict__ partial, unsigned long long *__restrict__ inv_part) {
+  extern __shared__ uint32_t s_bins[];
+  __shared__ unsigned long long s_inv;
+
+  // blockIdx -> (range, chunk): workgroups are dispatched to XCDs round
+  // robin, so XCD = blockIdx % 8. The ranges of one chunk get consecutive
+  // slots on one XCD.
+  const int b = blockIdx.x;
+  const int xcd = b & 7, slot = b >> 3;
+  const int r = slot % n_ranges;
+  const int c = (slot / n_ranges) * 8 + xcd;
+  if (c >= n_chunks) return;  // grid is rounded up to whole XCD rows
+
+  const uint32_t lo = (uint32_t)r * (uint32_t)range_bins;
+  const uint32_t nb = (uint32_t)min((int64_t)range_bins, (int64_t)V - lo);
+  for (uint32_t i = threadIdx.x; i < nb; i += kCountThreads) s_bins[i] = 0;
+  if (threadIdx.x == 0) s_inv = 0;
+  __syncthreads();
+
+  const uint64_t beg = (uint64_t)c * chunk_len;
+  const uint64_t end = beg + chunk_len < n ? beg + chunk_len : n;
+  unsigned long long inv = 0;
+  const bool tally = (r == 0);
+  if (beg < end) {
+    // chunk_len is a multiple of 4 and ids is 16-byte aligned.
+    const u32x4 *v4 = reinterpret_cast<const u32x4 *>(ids + beg);
+    const uint64_t n4 = (end - beg) >> 2;
+    constexpr int kUnroll = 4;
+    uint64_t i = threadIdx.x;
+    for (; i + (kUnroll - 1) * kCountThreads < n4; i += kUnroll * kCountThreads) {
+      u32x4 q[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) q[u] = load_stream16(v4 + i + u * kCountThreads);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int32_t a[4] = {(int32_t)q[u].x, (int32_t)q[u].y, (int32_t)q[u].z,
+                              (int32_t)q[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          count_one(a[e], lo, nb, s_bins);
+          if (tally) inv += (uint32_t)a[e] >= (uint32_t)V;
+        }
+      }
+    }
+    for (; i < n4; i += kCountThreads) {
+      const u32x4 q = load_stream16(v4 + i);
+      const int32_t a[4] = {(int32_t)q.x, (int32_t)q.y, (int32_t)q.z, (int32_t)q.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        count_one(a[e], lo, nb, s_bins);
+        if (tally) inv += (uint32_t)a[e] >= (uint32_t)V;
+      }
+    }
+    for (uint64_t j = beg + (n4 << 2) + threadIdx.x; j < end; j += kCountThreads) {
+      const int32_t a = ids[j];
+      count_one(a, lo, nb, s_bins);
+      if (tally) inv += (uint32_t)a >= (uint32_t)V;
+    }
+  }
+  if (tally && inv) atomicAdd(&s_inv, inv);
+  __syncthreads();
+
+  uint32_t *row = partial + (size_t)c * (size_t)V + lo;
+  for (uint32_t i = threadIdx.x; i < nb; i += kCountThreads) row[i] = s_bins[i];
+  if (tally && threadIdx.x == 0) inv_part[c] = s_inv;
+}
+
+__global__ __launch_bounds__(256) void count_reduce_kernel(
+    const uint32_t *__restrict__ partial, const unsigned long long *__restrict__ inv_part,
+    int32_t V, int32_t n_chunks, int accumulate, uint32_t *__restrict__ counts,
+    uint64_t *__restrict__ n_invalid) {
+  const int32_t v = blockIdx.x * 256 + threadIdx.x;
+  if (v < V) {
+    uint32_t s = accumulate ? counts[v] : 0u;
+    for (int c = 0; c < n_chunks; ++c) s += partial[(size_t)c * V + v];
+    counts[v] = s;
+  }
+  if (blockIdx.x == 0 && threadIdx.x < 64) {
+    unsigned long long t = 0;
+    for (int c = threadIdx.x; c < n_chunks; c += 64) t += inv_part[c];
+    for (int s = 32; s > 0; s >>= 1) t += __shfl_xor(t, s);
+    if (threadIdx.x == 0) *n_invalid = (accumulate ? *n_invalid : 0) + t;
+  }
+}
+
+}  // namespace
+
+CountPlan count_plan(uint64_t n, int32_t V) {
+  CountPlan p;
+  p.n_ranges = (V + kRangeBinsMax - 1) / kRangeBinsMax;
+  p.range_bins = (V + p.n_ranges - 1) / p.n_ranges;
+  // Chunks of ids: a multiple of 8 (whole chunks per XCD), at least 64k ids
+  // each, at most kMaxChunks. With 4 ranges that is 256 workgroups, one per
+  // CU; the partial table stays at kMaxChunks * V words.
+  int64_t c = (int64_t)((n + 65535) / 65536);
+  if (c > kMaxChunks) c = kMaxChunks;
+  if (c < 1) c = 1;
+  c = (c + 7) / 8 * 8;
+  p.n_chunks = (int32_t)c;
+  uint64_t len = (n + c - 1) / c;
+  p.chunk_len = (len + 3) / 4 * 4;
+  if (p.chunk_len == 0) p.chunk_len = 4;
+  p.partial_bytes = align_up((size_t)p.n_chunks * (size_t)V * 4, 256);
+  p.inv_bytes = align_up((size_t)p.n_chunks * 8, 256);
+  return p;
+}
+
+hipError_t launch_count(const int32_t *ids, uint64_t n, int32_t V,
+                        uint32_t *counts, int accumulate, uint64_t *n_invalid,
+                        void *ws, hipStream_t stream) {
+  const CountPlan p = count_plan(n, V);
+  uint32_t *partial = static_cast<uint32_t *>(ws);
+  unsigned long long *inv = reinterpret_cast<unsigned long long *>(
+      static_cast<char *>(ws) + p.partial_bytes);
+  const int slots = p.n_ranges * (p.n_chunks / 8);
+  const size_t lds = (size_t)p.range_bins * 4;
+  static bool lds_opt_in = false;  // the counting kernel needs > 64 KB of LDS
+  if (!lds_opt_in) {
+    hipError_t a = hipFuncSetAttribute((const void *)count_partial_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)(kRangeBinsMax * 4));
+    if (a != hipSuccess) return a;
+    lds_opt_in = true;
+  }
+  hipLaunchKernelGGL(count_partial_kernel, dim3(slots * 8), dim3(kCountThreads),
+                     lds, stream, ids, n, V, p.range_bins, p.n_ranges,
+                     p.n_chunks, p.chunk_len, partial, inv);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(count_reduce_kernel, dim3((V + 255) / 256), dim3(256), 0,
+                     stream, partial, inv, V, p.n_chunks, accumulate, counts,
+                     n_invalid);
+  return hipGetLastError();
+}
+
+}  // namespace vt

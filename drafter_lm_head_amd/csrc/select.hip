@@ -1,0 +1,268 @@
+// Top-V_high vocabulary selection (VocabTrim page, Implementation, Step 2;
+// FR-Spec notes, key design: keep the |V_high| most frequent tokens), for
+// gfx950.
+//
+// The order is (count descending, id ascending) over all V ids. The counts
+// (at most 608 KB) stay in L2, so one workgroup of 1024 threads does the
+// whole selection in one launch:
+//   1. radix select (11/11/10-bit digits) of the V_high-th largest count c*,
+//      and `need`, the number of ids with count c* that are kept;
+//   2. stable compaction, in id order, of the ids with count > c* and the
+//      first `need` ids with count == c*;
+//   3. stable LSD radix sort (8-bit digits) of the kept (count, id) pairs by
+//      descending count, over only the bits the largest count uses; since the
+//      pairs start in id order, equal counts stay in ascending id order;
+//   4. t2f, f2t and the two sums.
+#include "vt_internal.hpp"
+
+namespace vt {
+
+namespace {
+
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / kWave;
+
+struct SelShared {
+  uint32_t hist[2048];
+  uint32_t wsum[kSelWaves];
+  uint32_t total;
+  uint32_t digit, need;
+  unsigned long long r64[kSelWaves];
+  uint32_t r32[kSelWaves];
+  uint32_t dbase[256];
+  uint32_t drun[256];
+  uint32_t wcnt[kSelWaves][256];
+};
+
+// Exclusive prefix sum over the 1024 threads; *total receives the sum.
+__device__ uint32_t block_excl_scan(uint32_t x, SelShared &s, uint32_t *total) {
+  const int lane = __lane_id(), wave = threadIdx.x / kWave;
+  const uint32_t incl = wave_incl_scan(x);
+  if (lane == kWave - 1) s.wsum[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    const uint32_t y = lane < kSelWaves ? s.wsum[lane] : 0u;
+    const uint32_t yi = wave_incl_scan(y);
+    if (lane < kSelWaves) s.wsum[lane] = yi - y;
+    if (lane == kSelWaves - 1) s.total = yi;
+  }
+  __syncthreads();
+  const uint32_t r = s.wsum[wave] + incl - x;
+  *total = s.total;
+  __syncthreads();
+  return r;
+}
+
+__device__ unsigned long long block_sum_u64(unsigned long long x, SelShared &s) {
+  const int lane = __lane_id(), wave = threadIdx.x / kWave;
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  if (lane == 0) s.r64[wave] = x;
+  __syncthreads();
+  unsigned long long t = 0;
+  for (int w = 0; w < kSelWaves; ++w) t += s.r64[w];
+  __syncthreads();
+  return t;
+}
+
+__device__ uint32_t block_max_u32(uint32_t x, SelShared &s) {
+  const int lane = __lane_id(), wave = threadIdx.x / kWave;
+  for (int o = 32; o > 0; o >>= 1) x = max(x, (uint32_t)__shfl_xor(x, o));
+  if (lane == 0) s.r32[wave] = x;
+  __syncthreads();
+  uint32_t t = 0;
+  for (int w = 0; w < kSelWaves; ++w) t = max(t, s.r32[w]);
+  __syncthreads();
+  return t;
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_kernel(
+    const uint32_t *__restrict__ counts, int32_t V, int32_t V_high,
+    int32_t *__restrict__ t2f, int32_t *__restrict__ f2t,
+    uint64_t *__restrict__ sel_out, uint64_t *__restrict__ tot_out,
+    uint64_t *__restrict__ bufA, uint64_t *__restrict__ bufB) {
+  __shared__ SelShared s;
+  const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
+
+  // ---- 0. total and largest count
+  unsigned long long tot = 0;
+  uint32_t cmax = 0;
+  for (int32_t v = tid; v < V; v += kSelThreads) {
+    const uint32_t c = counts[v];
+    tot += c;
+    cmax = max(cmax, c);
+  }
+  tot = block_sum_u64(tot, s);
+  cmax = block_max_u32(cmax, s);
+
+  // ---- 1. radix select of c*, the V_high-th largest count
+  uint32_t prefix = 0, pmask = 0, need = (uint32_t)V_high;
+  const int shifts[3] = {21, 10, 0}, widths[3] = {11, 11, 10};
+  for (int p = 0; p < 3; ++p) {
+    const int sh = shifts[p];
+    const uint32_t nd = 1u << widths[p], dm = nd - 1;
+    for (uint32_t i = tid; i < nd; i += kSelThreads) s.hist[i] = 0;
+    __syncthreads();
+    for (int32_t v = tid; v < V; v += kSelThreads) {
+      const uint32_t c = counts[v];
+      if ((c & pmask) == prefix) atomicAdd(&s.hist[(c >> sh) & dm], 1u);
+    }
+    __syncthreads();
+    // Thread t owns digits d0 = nd-1-2t and d1 = d0-1 (largest first).
+    const int d0 = (int)nd - 1 - 2 * tid, d1 = d0 - 1;
+    const uint32_t h0 = d0 >= 0 ? s.hist[d0] : 0u, h1 = d1 >= 0 ? s.hist[d1] : 0u;
+    uint32_t tot_unused;
+    const uint32_t above = block_excl_scan(h0 + h1, s, &tot_unused);  // # with digit > d0
+    if (d0 >= 0 && above < need && above + h0 >= need) {
+      s.digit = (uint32_t)d0;
+      s.need = need - above;
+    } else if (d1 >= 0 && above + h0 < need && above + h0 + h1 >= need) {
+      s.digit = (uint32_t)d1;
+      s.need = need - above - h0;
+    }
+    __syncthreads();
+    prefix |= s.digit << sh;
+    pmask |= dm << sh;
+    need = s.need;
+    __syncthreads();
+  }
+  const uint32_t cstar = prefix;  // ids with count > c* all kept; `need` ties kept
+
+  // ---- 2. stable compaction in id order
+  const int32_t run = (V + kSelThreads - 1) / kSelThreads;
+  const int32_t vb = min(V, tid * run), ve = min(V, vb + run);
+  uint32_t n_gt = 0, n_eq = 0;
+  for (int32_t v = vb; v < ve; ++v) {
+    const uint32_t c = counts[v];
+    n_gt += c > cstar;
+    n_eq += c == cstar;
+  }
+  uint32_t scan_total;
+  const uint32_t eq_before = block_excl_scan(n_eq, s, &scan_total);
+  const uint32_t eq_take =
+      eq_before >= need ? 0u : min(n_eq, need - eq_before);
+  uint32_t pos = block_excl_scan(n_gt + eq_take, s, &scan_total);
+  {
+    uint32_t eq_rank = eq_before;
+    for (int32_t v = vb; v < ve; ++v) {
+      const uint32_t c = counts[v];
+      bool keep = c > cstar;
+      if (c == cstar) keep = eq_rank++ < need;
+      // pos < V_high always holds; the test keeps a logic error in bounds
+      if (keep && pos < (uint32_t)V_high) bufA[pos++] = ((uint64_t)c << 32) | (uint32_t)v;
+    }
+  }
+  __threadfence_block();
+  __syncthreads();
+
+  // ---- 3. stable LSD radix sort by descending count
+  const int nbits = cmax ? 32 - __clz(cmax) : 0;
+  const uint32_t kmask = nbits >= 32 ? 0xFFFFFFFFu : ((1u << nbits) - 1u);
+  const int passes = (nbits + 7) / 8;
+  uint64_t *src = bufA, *dst = bufB;
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  for (int p = 0; p < passes; ++p) {
+    const int sh = 8 * p;
+    for (int i = tid; i < 256; i += kSelThreads) {
+      s.hist[i] = 0;
+      s.drun[i] = 0;
+    }
+    __syncthreads();
+    for (int32_t i = tid; i < V_high; i += kSelThreads) {
+      const uint32_t key = (~(uint32_t)(src[i] >> 32)) & kmask;
+      atomicAdd(&s.hist[(key >> sh) & 255u], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) {  // exclusive scan of the 256 digit counts
+      uint32_t a[4], t = 0;
+      for (int j = 0; j < 4; ++j) {
+        a[j] = s.hist[lane * 4 + j];
+        t += a[j];
+      }
+      const uint32_t before = wave_incl_scan(t) - t;
+      uint32_t run_sum = before;
+      for (int j = 0; j < 4; ++j) {
+        s.dbase[lane * 4 + j] = run_sum;
+        run_sum += a[j];
+      }
+    }
+    __syncthreads();
+    for (int32_t base = 0; base < V_high; base += kSelThreads) {
+      const int32_t i = base + tid;
+      const bool valid = i < V_high;
+      uint64_t e = 0;
+      uint32_t dg = 0;
+      if (valid) {
+        e = src[i];
+        dg = (((~(uint32_t)(e >> 32)) & kmask) >> sh) & 255u;
+      }
+      uint64_t peers = __ballot(valid);
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const bool bit = (dg >> b) & 1u;
+        const uint64_t bb = __ballot(bit);
+        peers &= bit ? bb : ~bb;
+      }
+      for (int j = lane; j < 256; j += kWave) s.wcnt[wave][j] = 0;
+      const uint32_t rank = __popcll(peers & lt_mask);
+      if (valid && rank == 0) s.wcnt[wave][dg] = __popcll(peers);
+      __syncthreads();
+      if (tid < 256) {  // prefix over waves, per digit
+        uint32_t acc = s.drun[tid];
+        for (int w = 0; w < kSelWaves; ++w) {
+          const uint32_t t = s.wcnt[w][tid];
+          s.wcnt[w][tid] = acc;
+          acc += t;
+        }
+        s.drun[tid] = acc;
+      }
+      __syncthreads();
+      const uint32_t at = s.dbase[dg] + s.wcnt[wave][dg] + rank;
+      if (valid && at < (uint32_t)V_high) dst[at] = e;
+      __syncthreads();
+    }
+    __threadfence_block();
+    __syncthreads();
+    uint64_t *t = src;
+    src = dst;
+    dst = t;
+  }
+
+  // ---- 4. maps and sums
+  if (f2t)
+    for (int32_t v = tid; v < V; v += kSelThreads) f2t[v] = -1;
+  __threadfence_block();
+  __syncthreads();
+  unsigned long long sel = 0;
+  for (int32_t i = tid; i < V_high; i += kSelThreads) {
+    const uint64_t e = src[i];
+    const int32_t id = (int32_t)(uint32_t)e;
+    t2f[i] = id;
+    if (f2t && (uint32_t)id < (uint32_t)V) f2t[id] = i;
+    sel += e >> 32;
+  }
+  sel = block_sum_u64(sel, s);
+  if (tid == 0) {
+    *sel_out = sel;
+    *tot_out = tot;
+  }
+}
+
+}  // namespace
+
+size_t select_ws_bytes(int32_t V, int32_t V_high) {
+  (void)V;
+  return 2 * align_up((size_t)V_high * 8, 256);
+}
+
+hipError_t launch_select(const uint32_t *counts, int32_t V, int32_t V_high,
+                         int32_t *t2f, int32_t *f2t, uint64_t *sel,
+                         uint64_t *tot, void *ws, hipStream_t stream) {
+  uint64_t *a = static_cast<uint64_t *>(ws);
+  uint64_t *b = reinterpret_cast<uint64_t *>(static_cast<char *>(ws) +
+                                             align_up((size_t)V_high * 8, 256));
+  hipLaunchKernelGGL(select_kernel, dim3(1), dim3(kSelThreads), 0, stream,
+                     counts, V, V_high, t2f, f2t, sel, tot, a, b);
+  return hipGetLastError();
+}
+
+}  // namespace vt

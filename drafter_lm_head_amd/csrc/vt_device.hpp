@@ -1,0 +1,175 @@
+// Device helpers shared by the gfx950 kernels: wave64 reductions on DPP,
+// order-preserving 64-bit top-k keys, bitonic sort across a wave, and
+// cross-workgroup release/acquire.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vt {
+
+constexpr int kWave = 64;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- loads
+// Streaming 16-byte load that should not displace reused lines.
+__device__ __forceinline__ u32x4 load_stream16(const u32x4 *p) {
+  return __builtin_nontemporal_load(p);
+}
+
+// fp32 += a.lo*b.lo + a.hi*b.hi on two packed bf16 pairs (v_dot2c_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c,
+                                         false);
+}
+
+__device__ __forceinline__ float dot8_bf16(u32x4 a, u32x4 b, float c) {
+  c = dot2_bf16(a.x, b.x, c);
+  c = dot2_bf16(a.y, b.y, c);
+  c = dot2_bf16(a.z, b.z, c);
+  c = dot2_bf16(a.w, b.w, c);
+  return c;
+}
+
+// ---------------------------------------------------------- DPP shuffles
+// GFX9 DPP controls used below.
+enum : int {
+  kDppQuadXor1 = 0xB1,      // quad_perm [1,0,3,2]
+  kDppQuadXor2 = 0x4E,      // quad_perm [2,3,0,1]
+  kDppRowHalfMirror = 0x141,
+  kDppRowMirror = 0x140,
+};
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF,
+                                               false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(x)));
+}
+
+__device__ __forceinline__ float readlane_f32(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int lane) {
+  uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, lane);
+  uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Sum over the 64 lanes in a fixed order; every lane must be active. The
+// result is wave-uniform.
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp_f32<kDppQuadXor1>(x);
+  x += dpp_f32<kDppQuadXor2>(x);
+  x += dpp_f32<kDppRowHalfMirror>(x);
+  x += dpp_f32<kDppRowMirror>(x);
+  return (readlane_f32(x, 0) + readlane_f32(x, 16)) +
+         (readlane_f32(x, 32) + readlane_f32(x, 48));
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_f32<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp_f32<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp_f32<kDppRowHalfMirror>(x));
+  x = fmaxf(x, dpp_f32<kDppRowMirror>(x));
+  return fmaxf(fmaxf(readlane_f32(x, 0), readlane_f32(x, 16)),
+               fmaxf(readlane_f32(x, 32), readlane_f32(x, 48)));
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+  uint32_t lo = dpp_u32<CTRL>((uint32_t)x);
+  uint32_t hi = dpp_u32<CTRL>((uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) {
+  return a > b ? a : b;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+  x = max_u64(x, dpp_u64<kDppQuadXor1>(x));
+  x = max_u64(x, dpp_u64<kDppQuadXor2>(x));
+  x = max_u64(x, dpp_u64<kDppRowHalfMirror>(x));
+  x = max_u64(x, dpp_u64<kDppRowMirror>(x));
+  return max_u64(max_u64(readlane_u64(x, 0), readlane_u64(x, 16)),
+                 max_u64(readlane_u64(x, 32), readlane_u64(x, 48)));
+}
+
+// Inclusive prefix sum over lanes (lane i gets x_0 + ... + x_i).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int s = 1; s < kWave; s <<= 1) {
+    uint32_t y = __shfl_up(x, s);
+    if (lane >= s) x += y;
+  }
+  return x;
+}
+
+// ------------------------------------------------------------ top-k keys
+// A key orders candidates by logit (larger first) and, among equal logits,
+// by full token id (lower first): high word = order-preserving image of the
+// fp32 logit, low word = ~full_id. Key 0 is below every real candidate and
+// marks an empty slot.
+__device__ __forceinline__ uint32_t ord_from_f32(float z) {
+  if (z == 0.0f) z = 0.0f;  // -0 and +0 are the same logit
+  uint32_t u = __float_as_uint(z);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float f32_from_ord(uint32_t o) {
+  uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+  return __uint_as_float(u);
+}
+__device__ __forceinline__ uint64_t make_key(float z, int32_t full_id) {
+  return ((uint64_t)ord_from_f32(z) << 32) | (uint32_t)(~(uint32_t)full_id);
+}
+__device__ __forceinline__ float key_logit(uint64_t key) {
+  return f32_from_ord((uint32_t)(key >> 32));
+}
+__device__ __forceinline__ int32_t key_id(uint64_t key) {
+  return (int32_t)(~(uint32_t)key);
+}
+
+// Sorts one key per lane so that lane 0 holds the largest (bitonic network).
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int size = 2; size <= kWave; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      uint64_t other = __shfl_xor(key, stride);
+      const bool lower = (lane & stride) == 0;
+      const bool desc = (lane & size) == 0;
+      key = (lower == desc) ? max_u64(key, other)
+                            : (key < other ? key : other);
+    }
+  }
+  return key;
+}
+
+// -------------------------------------------------- cross-workgroup order
+// Publishes this workgroup's global writes and takes a ticket: returns the
+// number of workgroups that arrived before it. Must be called by every
+// thread of the workgroup (it contains a barrier); the return value is
+// uniform.
+__device__ __forceinline__ uint32_t arrive(uint32_t *counter, uint32_t *s_slot) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    *s_slot = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  const uint32_t t = *s_slot;
+  __threadfence();  // acquire side: see what the earlier arrivals published
+  return t;
+}
+
+}  // namespace vt

@@ -1,0 +1,55 @@
+// Internal interface between the C ABI (api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "vt_device.hpp"
+
+namespace vt {
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// gfx950 has 160 KB of LDS per CU; one counting workgroup uses up to
+// kRangeBinsMax 32-bit bins of it.
+constexpr int kRangeBinsMax = 38912;  // 152 KB
+constexpr int kMaxChunks = 64;        // rows of the partial histogram table
+
+struct CountPlan {
+  int32_t n_ranges, range_bins, n_chunks;
+  uint64_t chunk_len;
+  size_t partial_bytes, inv_bytes;
+};
+CountPlan count_plan(uint64_t n, int32_t V);
+hipError_t launch_count(const int32_t *ids, uint64_t n, int32_t V,
+                        uint32_t *counts, int accumulate, uint64_t *n_invalid,
+                        void *ws, hipStream_t stream);
+
+size_t select_ws_bytes(int32_t V, int32_t V_high);
+hipError_t launch_select(const uint32_t *counts, int32_t V, int32_t V_high,
+                         int32_t *t2f, int32_t *f2t, uint64_t *sel,
+                         uint64_t *tot, void *ws, hipStream_t stream);
+
+hipError_t launch_gather(const uint16_t *W, int32_t V, int32_t d,
+                         const int32_t *t2f, int32_t V_high, uint16_t *W_trim,
+                         uint32_t *n_bad, hipStream_t stream);
+
+// Draft head: tiles of kTileRows rows of W_trim; tile partials are merged
+// in groups, then the group results are merged once.
+constexpr int kTileRows = 64;
+struct HeadPlan {
+  int32_t tiles, group_size, groups;
+  size_t off_tile_keys, off_tile_ms, off_group_keys, off_group_ms;
+  size_t bytes;
+};
+HeadPlan head_plan(int32_t M, int32_t V_high, int32_t k);
+hipError_t launch_draft_head(const uint16_t *h, int32_t M, int32_t d,
+                             const uint16_t *W_trim, int32_t V_high,
+                             const int32_t *t2f, int32_t k, int32_t *full_ids,
+                             float *probs, void *ws, hipStream_t stream);
+hipError_t launch_head_logits(const uint16_t *h, int32_t M, int32_t d,
+                              const uint16_t *W_trim, int32_t V_high,
+                              float *logits, hipStream_t stream);
+
+}  // namespace vt

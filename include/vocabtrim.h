@@ -1,0 +1,178 @@
+/*
+ * vocabtrim.h - C ABI of the frequency-ranked drafter LM head for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method (two pages describe it):
+ *   [VT] "VocabTrim: Memory-Efficient Vocabulary Pruning for Speculative
+ *        Decoding" (skill page; Implementation, Steps 1-4; Practical
+ *        Guidance; pitfalls).
+ *   [FR] "FR-Spec: Accelerating Large-Vocabulary Language Models via
+ *        Frequency-Ranked Speculative Sampling" (paper notes; Method,
+ *        overall framework and key design).
+ * A drafter's LM head W[V, d] is cut down to the V_high most frequent token
+ * ids. Preparation counts ids, ranks them and gathers the kept rows into
+ * W_trim[V_high, d]; every draft step then computes the logits of the kept
+ * rows only, a softmax over the kept subset, the k best tokens per draft row,
+ * and maps them back to full-vocabulary ids.
+ *
+ * Conventions shared by every call:
+ *   - Pointers named as device pointers must point to device memory of the
+ *     current HIP device (e.g. torch tensors); they are owned by the caller,
+ *     contiguous and row-major. bfloat16 values are passed as uint16_t bit
+ *     patterns. Device pointers to 16-byte vectors must be 16-byte aligned
+ *     where stated.
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL is the default stream) and never blocks the host. The library
+ *     allocates no memory: scratch space is passed in as a workspace whose
+ *     size the matching *_workspace_size call returns.
+ *   - Arguments are validated on the host before any HIP call. A call that
+ *     returns an error status has launched nothing and written nothing.
+ *     VT_ERR_HIP means a launch failed; hipGetLastError() was cleared.
+ *   - Calls are not synchronised with each other except by stream order.
+ *     Two calls that share a workspace must run in stream order (not
+ *     concurrently on different streams).
+ */
+#ifndef VOCABTRIM_H
+#define VOCABTRIM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VT_ABI_VERSION 1
+
+/* Limits of this build. */
+#define VT_K_MAX 64           /* top-k per draft row                        */
+#define VT_M_MAX 64           /* draft rows per vt_draft_head call           */
+#define VT_D_MAX 8192         /* hidden size; d must also be a multiple of 8 */
+#define VT_VHIGH_MAX 262144   /* kept vocabulary per vt_draft_head call     */
+
+typedef enum {
+    VT_OK = 0,
+    VT_ERR_INVALID_ARG = -1,  /* null/misaligned pointer or size out of range */
+    VT_ERR_UNSUPPORTED = -2,  /* valid request beyond this build's limits     */
+    VT_ERR_WORKSPACE = -3,    /* workspace missing, misaligned or too small   */
+    VT_ERR_HIP = -4           /* a HIP launch or query failed                 */
+} vt_status;
+
+/* Static text for a status code (never NULL). */
+const char *vt_status_string(int status);
+
+/* VT_ABI_VERSION of the loaded library. */
+int vt_version(void);
+
+/* ------------------------------------------------------------------ count
+ * Token-id histogram: [VT] Step 1 counts every id the drafter samples on
+ * calibration data; [FR] key design counts token frequencies over a corpus.
+ *
+ *   counts[v] (+)= number of i < n with ids[i] == v, for 0 <= v < V
+ *   n_invalid (+)= number of i < n with ids[i] < 0 or ids[i] >= V
+ *
+ * ids       device, int32[n], 16-byte aligned (may be NULL when n == 0)
+ * n         number of ids, n <= UINT32_MAX
+ * V         full vocabulary, 1 <= V < 2^31
+ * counts    device, uint32[V]; overwritten, or added to when accumulate != 0
+ * n_invalid device, uint64[1]; overwritten, or added to when accumulate != 0
+ * ws        device workspace of at least vt_count_freq_workspace_size(n, V)
+ *           bytes, 256-byte aligned; no initial contents required.
+ * Counts are exact. With accumulate the caller keeps each count below 2^32
+ * (it wraps modulo 2^32 otherwise). Ids out of range are never counted and
+ * cause no out-of-bounds access. */
+size_t vt_count_freq_workspace_size(uint64_t n, int32_t V);
+int vt_count_freq(const int32_t *ids, uint64_t n, int32_t V, uint32_t *counts,
+                  int accumulate, uint64_t *n_invalid, void *ws,
+                  size_t ws_bytes, void *stream);
+
+/* ----------------------------------------------------------------- select
+ * Top-V_high vocabulary and both maps: [VT] Step 2 sorts ids by count, keeps
+ * the first target_vocab_size, builds trimmed_to_full / full_to_trimmed and
+ * the coverage; [FR] key design keeps the |V_high| most frequent tokens.
+ *
+ * All V ids are ranked by (count descending, id ascending); ids never seen
+ * (count 0) rank last by id. Then
+ *   t2f[i]       = id at rank i, for i < V_high (trimmed_to_full)
+ *   f2t[t2f[i]]  = i, and -1 for every id that is not kept (full_to_trimmed)
+ *   sel_sum      = sum of counts[t2f[i]],  tot_sum = sum of counts[v]
+ * Coverage is sel_sum / tot_sum (the caller divides; tot_sum == 0 means no
+ * id was counted).
+ *
+ * counts  device, uint32[V]
+ * V, V_high  1 <= V_high <= V < 2^31
+ * t2f     device, int32[V_high]
+ * f2t     device, int32[V], or NULL to skip it
+ * sel_sum, tot_sum  device, uint64[1] each
+ * ws      device workspace of vt_select_vocab_workspace_size(V, V_high)
+ *         bytes, 256-byte aligned; no initial contents required.
+ * The result is unique (the order is total), so it is bit-exact. */
+size_t vt_select_vocab_workspace_size(int32_t V, int32_t V_high);
+int vt_select_vocab(const uint32_t *counts, int32_t V, int32_t V_high,
+                    int32_t *t2f, int32_t *f2t, uint64_t *sel_sum,
+                    uint64_t *tot_sum, void *ws, size_t ws_bytes,
+                    void *stream);
+
+/* ----------------------------------------------------------------- gather
+ * Trimmed head: [VT] Step 3 keeps the head rows of the kept ids; [FR] key
+ * design shrinks the head from d x 128k to d x 32k.
+ *
+ *   W_trim[i, :] = W[t2f[i], :]   for i < V_high  (bit copy)
+ *
+ * W       device, bf16[V, d], 16-byte aligned;  d % 8 == 0, 8 <= d <= VT_D_MAX
+ * t2f     device, int32[V_high] (from vt_select_vocab or the caller)
+ * W_trim  device, bf16[V_high, d], 16-byte aligned; must not overlap W
+ * n_bad   device uint32[1] or NULL. A t2f entry outside [0, V) is not read
+ *         through: its output row is filled with zeros and, when n_bad is
+ *         given, counted into *n_bad (which the call first sets to 0). */
+int vt_gather_head(const uint16_t *W, int32_t V, int32_t d,
+                   const int32_t *t2f, int32_t V_high, uint16_t *W_trim,
+                   uint32_t *n_bad, void *stream);
+
+/* ------------------------------------------------------------- draft head
+ * One draft step of the trimmed head: [VT] Step 4 (logits of the trimmed
+ * head, softmax over the trimmed vocabulary, pick, remap trimmed -> full id
+ * with a table lookup as the page's pitfalls advise) and [FR] key design
+ * (the head and its softmax cover the subset only).
+ *
+ * For every draft row m < M:
+ *   z[m, j]   = sum_t h[m, t] * W_trim[j, t]   (bf16 inputs, fp32 sums)
+ *   mu, S     = max_j z[m, j],  sum_j exp(z[m, j] - mu)   over j < V_high
+ *   the k largest z[m, j] in rank order (equal logits: lower full id first)
+ *   full_ids[m, r] = t2f[j_r],   probs[m, r] = exp(z[m, j_r] - mu) / S
+ * The pick is a deterministic top-k; probs are subset-softmax values (not
+ * renormalised over the k picks); temperature is 1. The logits never leave
+ * the chip: one kernel streams W_trim once and merges per-tile partial
+ * results in a fixed order, so repeated calls give identical bits.
+ *
+ * h         device, bf16[M, d], 16-byte aligned; 1 <= M <= VT_M_MAX
+ * d         d % 8 == 0, 8 <= d <= VT_D_MAX
+ * W_trim    device, bf16[V_high, d], 16-byte aligned; 1 <= V_high <= VT_VHIGH_MAX
+ * t2f       device, int32[V_high]; only copied to the output and used to
+ *           break ties, never used as an address
+ * k         1 <= k <= min(V_high, VT_K_MAX)
+ * full_ids  device, int32[M, k];  probs  device, float[M, k]
+ * ws        device workspace of vt_draft_head_workspace_size(M, V_high, d, k)
+ *           bytes, 256-byte aligned. It must be zero-filled once before its
+ *           first use; every call leaves its counters at zero again. */
+size_t vt_draft_head_workspace_size(int32_t M, int32_t V_high, int32_t d,
+                                    int32_t k);
+int vt_draft_head(const uint16_t *h, int32_t M, int32_t d,
+                  const uint16_t *W_trim, int32_t V_high, const int32_t *t2f,
+                  int32_t k, int32_t *full_ids, float *probs, void *ws,
+                  size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------- logits (checks)
+ * The trimmed logits alone, z[m, j] as defined for vt_draft_head, written to
+ * logits (device, float[M, V_high]). For parity diagnostics: it writes the
+ * M x V_high logits to memory, which vt_draft_head never does.
+ * Same argument rules as vt_draft_head. */
+int vt_head_logits(const uint16_t *h, int32_t M, int32_t d,
+                   const uint16_t *W_trim, int32_t V_high, float *logits,
+                   void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VOCABTRIM_H */

@@ -52,11 +52,17 @@ def _load():
             lib.or_softmax.argtypes = [P, i32, i32, P, P, P]
             lib.or_topk.argtypes = [P, P, i32, i32, i32, P, P]
             lib.or_draft_head.argtypes = [P, i32, i32, P, i32, P, i32, P, P, P, P, P]
-            for f in (lib.or_count, lib.or_select, lib.or_gather, lib.or_logits,
+            lib.or_threads.argtypes = []
+            for f in (lib.or_threads, lib.or_count, lib.or_select, lib.or_gather, lib.or_logits,
                       lib.or_softmax, lib.or_topk, lib.or_draft_head):
                 f.restype = C.c_int
             _lib = lib
     return _lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().or_threads())
 
 
 def _p(a: np.ndarray | None):

@@ -34,6 +34,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define OR_OK 0
 #define OR_BAD -1
@@ -49,6 +52,16 @@ static double bf16_value(uint16_t b)
 }
 
 int or_version(void) { return 1; }
+
+/* Threads the OpenMP loops use (1 when built without OpenMP). */
+int or_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* Step 1 of [VT] (count every sampled token id) and [FR]'s corpus frequency
  * statistics: counts[v] = number of i with ids[i] == v.

@@ -162,13 +162,11 @@ def hidden_states(M: int, d: int, rng: np.random.Generator,
 def _ids_cached(n: int, V: int, s: float, permute: bool, seed: int) -> np.ndarray:
     g_ids, g_perm, _, _ = streams(seed)
     perm = g_perm.permutation(V).astype(np.int32) if permute else None
-    a = zipf_ids(n, V, s, g_ids, perm)
-    a.setflags(write=False)
-    return a
+    return zipf_ids(n, V, s, g_ids, perm)
 
 
 def make_ids(w: Workload, n: int | None = None) -> np.ndarray:
-    """The workload's id stream (read-only, cached per process)."""
+    """The workload's id stream (cached per process; do not modify it)."""
     return _ids_cached(int(w.n_ids if n is None else n), w.V, w.zipf_s,
                        w.permute, w.seed)
 

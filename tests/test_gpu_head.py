@@ -1,0 +1,179 @@
+"""GPU parity of the draft head through the C ABI (VocabTrim page,
+Implementation, Step 4; FR-Spec notes, key design): trimmed logits, subset
+softmax, per-row top-k and the trimmed -> full remap, against the fp64 CPU
+oracle under the acceptance rule in tests/parity.py."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+from parity import (DEV, check_picks, logit_bound, to_dev_bf16, to_dev_i32)
+
+
+@pytest.fixture(scope="module")
+def dlh():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import drafter_lm_head_amd as m
+    return m
+
+
+def rand_case(seed, M, d, V_high, V=None, hscale=1.0):
+    rng = np.random.default_rng(seed)
+    V = V or max(V_high, 2 * V_high)
+    W = synth.bf16_bits_from_f32(rng.standard_normal((V_high, d), dtype=np.float32) * np.float32(0.02))
+    h = synth.bf16_bits_from_f32(rng.standard_normal((M, d), dtype=np.float32) * np.float32(hscale))
+    t2f = rng.permutation(V)[:V_high].astype(np.int32)
+    return h, W, t2f
+
+
+def run_head(dlh, h, W, t2f, k):
+    ids, probs = dlh.vt_draft_head(to_dev_bf16(h), to_dev_bf16(W), to_dev_i32(t2f), k)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), probs.cpu().numpy()
+
+
+def check_case(dlh, h, W, t2f, k):
+    ids_g, probs_g = run_head(dlh, h, W, t2f, k)
+    ids_o, probs_o, (z_o, _, _) = oracle.draft_head(h, W, t2f, k, want_logits=True)
+    return check_picks(ids_g, probs_g, z_o, t2f, k, ids_o)
+
+
+def test_tiny_pipeline_matches_oracle(dlh):
+    w = synth.WORKLOADS["tiny"]
+    W = synth.make_weights(w)
+    c, _ = oracle.count(synth.make_ids(w), w.V)
+    t2f, _, _, _ = oracle.select(c, w.V_high)
+    Wt = oracle.gather(W, t2f)
+    for scale in (1.0, 16.0):       # flat and peaked subset softmax
+        h = synth.make_hidden(w, scale=scale)
+        check_case(dlh, h, Wt, t2f, w.k)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 16])
+def test_draft_rows(dlh, M):
+    h, W, t2f = rand_case(M, M, 512, 3000)
+    check_case(dlh, h, W, t2f, 10)
+
+
+@pytest.mark.parametrize("V_high", [1, 10, 63, 64, 65, 1000, 4097])
+def test_ragged_vocab(dlh, V_high):
+    h, W, t2f = rand_case(V_high, 2, 256, V_high)
+    check_case(dlh, h, W, t2f, min(10, V_high))
+
+
+@pytest.mark.parametrize("d", [8, 72, 256, 520, 1000, 2048, 3584, 4096, 6144, 8192])
+def test_hidden_sizes(dlh, d):
+    h, W, t2f = rand_case(d, 1, d, 777)
+    check_case(dlh, h, W, t2f, 10)
+
+
+@pytest.mark.parametrize("k", [1, 2, 31, 32, 63, 64])
+def test_k_range(dlh, k):
+    h, W, t2f = rand_case(100 + k, 2, 256, 5000, hscale=4.0)
+    check_case(dlh, h, W, t2f, k)
+
+
+def test_exact_ties_break_to_lower_full_id(dlh):
+    # All rows equal: every logit ties, so the picks are the k smallest full ids.
+    rng = np.random.default_rng(5)
+    d, V_high, k = 64, 700, 12
+    row = synth.bf16_bits_from_f32(rng.standard_normal(d, dtype=np.float32))
+    W = np.tile(row, (V_high, 1))
+    h = synth.bf16_bits_from_f32(rng.standard_normal((2, d), dtype=np.float32))
+    t2f = rng.permutation(100_000)[:V_high].astype(np.int32)
+    ids_g, probs_g = run_head(dlh, h, W, t2f, k)
+    want = np.sort(t2f)[:k]
+    for m in range(2):
+        np.testing.assert_array_equal(ids_g[m], want)
+        np.testing.assert_allclose(probs_g[m], 1.0 / V_high, rtol=1e-5)
+
+
+def test_hand_worked_example(dlh):
+    import json, os
+    from conftest import GOLDEN
+    g = json.load(open(os.path.join(GOLDEN, "hand_head.json")))
+    # d = 4 is below the 8-element vector width: pad with zero columns.
+    h = np.zeros((2, 8), np.float32)
+    h[:, :4] = g["h"]
+    W = np.zeros((5, 8), np.float32)
+    W[:, :4] = g["W_trim"]
+    ids_g, probs_g = run_head(dlh, synth.bf16_bits_from_f32(h), synth.bf16_bits_from_f32(W),
+                              np.array(g["t2f"], np.int32), g["k"])
+    assert ids_g.tolist() == g["full_ids"]
+    np.testing.assert_allclose(probs_g, np.array(g["probs"]), rtol=2e-6)
+
+
+def test_determinism_and_counter_reset(dlh):
+    h, W, t2f = rand_case(7, 3, 1024, 20000)
+    hd, Wd, td = to_dev_bf16(h), to_dev_bf16(W), to_dev_i32(t2f)
+    M, d = h.shape
+    n = dlh.vt_draft_head_workspace_size(M, 20000, d, 10)
+    ws = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    ref = None
+    for _ in range(50):
+        ids, probs = dlh.vt_draft_head(hd, Wd, td, 10, ws=ws)
+        cur = (ids.cpu().numpy().tobytes(), probs.cpu().numpy().tobytes())
+        if ref is None:
+            ref = cur
+        assert cur == ref
+    torch.cuda.synchronize()
+    assert int(ws[:256].sum().item()) == 0     # tickets back at zero
+
+
+def test_full_vocab_equals_untrimmed_head(dlh):
+    # V_high = V with the frequency-ranked permutation gives the same picks as
+    # the untrimmed head with the identity map.
+    w = synth.WORKLOADS["tiny"]
+    W = synth.make_weights(w)
+    h = synth.make_hidden(w, M=2, scale=4.0)
+    c, _ = oracle.count(synth.make_ids(w), w.V)
+    t2f, _, _, _ = oracle.select(c, w.V)
+    ident = np.arange(w.V, dtype=np.int32)
+    ids_t, p_t = run_head(dlh, h, oracle.gather(W, t2f), t2f, 16)
+    ids_u, p_u = run_head(dlh, h, W, ident, 16)
+    np.testing.assert_array_equal(ids_t, ids_u)
+    np.testing.assert_allclose(p_t, p_u, rtol=1e-5)
+
+
+def test_logits_within_fp32_bound(dlh):
+    h, W, t2f = rand_case(9, 2, 4096, 2000)
+    z_g = dlh.vt_head_logits(to_dev_bf16(h), to_dev_bf16(W)).cpu().numpy().astype(np.float64)
+    z_o = oracle.logits(h, W)
+    assert np.all(np.abs(z_g - z_o) <= logit_bound(h, W))
+
+
+@pytest.fixture(scope="module")
+def llama(dlh):
+    # The LLaMA-3-8B drafter head as the method builds it: 1e8 Zipf ids,
+    # counted and ranked by the oracle, rows gathered from a seeded W.
+    w = synth.WORKLOADS["llama3_8b"]
+    W = synth.make_weights(w)
+    c, _ = oracle.count(synth.make_ids(w), w.V)
+    t2f, _, _, _ = oracle.select(c, w.V_high)
+    Wt = oracle.gather(W, t2f)
+    del W
+    return w, Wt, t2f
+
+
+@pytest.mark.parametrize("M,scale", [(1, 1.0), (1, 16.0), (4, 1.0)])
+def test_llama_head_full_size(dlh, llama, M, scale):
+    w, Wt, t2f = llama
+    h = synth.make_hidden(w, M=M, scale=scale)
+    worst = check_case(dlh, h, Wt, t2f, w.k)
+    print("worst", worst)
+
+
+def test_llama_logits_bound(dlh, llama):
+    w, Wt, t2f = llama
+    h = synth.make_hidden(w)
+    z_g = dlh.vt_head_logits(to_dev_bf16(h), to_dev_bf16(Wt)).cpu().numpy().astype(np.float64)
+    z_o = oracle.logits(h, Wt)
+    err = np.abs(z_g - z_o)
+    assert np.all(err <= logit_bound(h, Wt))
+    print("max |dz|", err.max())
