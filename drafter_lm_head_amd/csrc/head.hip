@@ -9,116 +9,284 @@
 //   * the tile's logits go to LDS; per draft row one wave sorts the 64
 //     (logit, full id) keys, and writes the tile's top-k keys and its
 //     softmax partial (max, sum of exp(z - max)) to the workspace;
-//   * tiles are grouped; the last workgroup of a group to finish (atomic
-//     ticket) merges the group's partials, and the last group merger merges
-//     the groups and writes full_ids and probs. Every merge runs in a fixed
-//     order, so results do not depend on scheduling.
+//   * the workgroup that finishes last (atomic ticket) reads every tile's
+//     partial once and merges them: the online-softmax partials in a fixed
+//     order, the keys by a threshold filter and a sort, so results do not
+//     depend on scheduling; it writes full_ids and probs.
 // The kernel is bound by HBM bandwidth: it moves 2 * V_high * d bytes of
 // W_trim and does 2 * M * V_high * d flops.
 #include "vt_internal.hpp"
-
-#ifndef VT_GEMV_WAVES
-#define VT_GEMV_WAVES 4
-#endif
-#ifndef VT_GEMV_ROWS
-#define VT_GEMV_ROWS 4
-#endif
+#include "vocabtrim.h"
 
 namespace vt {
 
 namespace {
+
+constexpr int kGroups = 64;  // tile groups whose maxima bound the k-th key
 
 struct HeadArgs {
   const u32x4 *h;        // [M, c16]
   const u32x4 *W;        // [V_high, c16]
   const int32_t *t2f;    // [V_high]
   int32_t M, c16, V_high, k;
-  int32_t tiles, group_size, groups;
-  uint64_t *tile_keys;   // [M][tiles][k]
-  float2 *tile_ms;       // [M][tiles]
-  uint64_t *group_keys;  // [M][groups][k]
-  float2 *group_ms;      // [M][groups]
-  uint32_t *counters;    // [groups + 1], zero between calls
+  int32_t tiles;
+  uint64_t *tile_keys;   // [M][tiles][k], published
+  uint64_t *tile_ms;     // [M][tiles], (bits(S) << 32) | bits(max), published
+  uint64_t *group_max;   // [M][kGroups]: largest tile head per tile group
+  uint64_t *group_kth;   // [M][kGroups]: largest tile k-th key per group
+  int32_t tiles_per_group;
+  uint32_t *counter;     // tickets, zero between calls
   int32_t *full_ids;     // [M][k]
   float *probs;          // [M][k]
   float *logits;         // [M][V_high], logits-only variant
 };
 
-// Merges P <= 64 parts. Part p has its k largest keys in descending order at
-// lists[p * k ...] and its softmax partial ms[p] = (max, sum of exp(z - max)).
-// Returns the overall rank-`lane` key for lanes < k; *mu and *S receive the
-// merged max and sum. The k-th largest key overall is at least T, the
-// largest of the parts' k-th keys, so only keys >= T can be picked; they are
-// collected and sorted in one wave. If more than 64 keys tie above T, the
-// parts' heads are merged one rank at a time instead.
-__device__ uint64_t merge_parts(const uint64_t *lists, const float2 *ms, int P,
-                                int k, uint64_t *s_buf, float *mu, float *S) {
-  const int lane = __lane_id();
-  const float2 p = lane < P ? ms[lane] : make_float2(-INFINITY, 0.f);
-  const float m = wave_max(p.x);
-  *S = wave_sum(lane < P ? p.y * __expf(p.x - m) : 0.f);
-  *mu = m;
+__device__ __forceinline__ uint64_t pack_ms(float mu, float S) {
+  return ((uint64_t)__float_as_uint(S) << 32) | __float_as_uint(mu);
+}
+__device__ __forceinline__ float ms_max(uint64_t v) { return __uint_as_float((uint32_t)v); }
+__device__ __forceinline__ float ms_sum(uint64_t v) { return __uint_as_float((uint32_t)(v >> 32)); }
 
-  const uint64_t T =
-      wave_max_u64(lane < P ? lists[(size_t)lane * k + (k - 1)] : 0ull);
-  const int n = P * k;
-  const uint64_t lt = (1ull << lane) - 1ull;
-  uint32_t found = 0;
-  for (int j0 = 0; j0 < n; j0 += 4 * kWave) {
-    uint64_t v[4];
+constexpr int kMaxTiles = VT_VHIGH_MAX / kTileRows;
+
+constexpr int kCandCap = 1024;   // survivors the final merge can hold
+
+template <int WAVES>
+struct alignas(16) MergeShared {
+  alignas(16) uint64_t cand[kCandCap];       // survivors of the threshold
+  alignas(16) uint64_t sc[2][kWave];         // rank inputs / outputs
+  uint32_t prank[4][4][kWave];               // partial ranks
+  unsigned long long kmax, T;
+  uint32_t cnt;
+  float f[WAVES];
+};
+
+// Ranks (0 = largest) of NR rows of 64 keys in LDS, keys[r * 64 + lane],
+// counted by up to 4 waves per row: wave w takes row w % NR and a quarter
+// (half, whole) of the keys to compare against, so the latency of a rank
+// is that of 16 to 64 compares. Keys must be distinct apart from 0. Every
+// thread must call it (it has a barrier); the rank of keys[w * 64 + lane]
+// is returned to wave w < NR.
+template <int WAVES, int NR>
+__device__ __forceinline__ uint32_t block_rank(const uint64_t *keys,
+                                               uint32_t *prank) {
+  typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+  constexpr int P = (WAVES / NR) < 4 ? (WAVES / NR) : 4;
+  constexpr int SPAN = kWave / P;
+  static_assert(P >= 1 && SPAN % 2 == 0, "parts must split 64 keys evenly");
+  const int lane = __lane_id(), wave = threadIdx.x / kWave;
+  if (wave < NR * P) {
+    const int r = wave % NR, part = wave / NR;
+    const uint64_t v = keys[r * kWave + lane];
+    const uint64_t *kr = keys + r * kWave + part * SPAN;
+    uint32_t c = 0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int idx = j0 + u * kWave + lane;
-      v[u] = idx < n ? lists[idx] : 0ull;
+    for (int j = 0; j < SPAN; j += 2) {
+      const u64x2 q = *reinterpret_cast<const u64x2 *>(kr + j);
+      c += q.x > v;
+      c += q.y > v;
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const bool take = v[u] != 0ull && v[u] >= T;
-      const uint64_t bal = __ballot(take);
-      const uint32_t pos = found + (uint32_t)__popcll(bal & lt);
-      if (take && pos < kWave) s_buf[pos] = v[u];
-      found += (uint32_t)__popcll(bal);
-    }
+    prank[(part * NR + r) * kWave + lane] = c;
   }
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  uint64_t key = 0;
-  if (found <= (uint32_t)kWave) {
-    key = lane < (int)found ? s_buf[lane] : 0ull;
-    key = wave_sort_desc(key);
-  } else {
-    int pos = 0;
-    uint64_t head = lane < P ? lists[(size_t)lane * k] : 0ull;
-    for (int r = 0; r < k; ++r) {
-      const uint64_t mx = wave_max_u64(head);
-      if (lane == r) key = mx;
-      const uint64_t win = __ballot(lane < P && head == mx);
-      if (lane == __ffsll((unsigned long long)win) - 1) {
-        ++pos;
-        head = pos < k ? lists[(size_t)lane * k + pos] : 0ull;
+  __syncthreads();
+  uint32_t rank = 0;
+  if (wave < NR)
+#pragma unroll
+    for (int p = 0; p < P; ++p) rank += prank[(p * NR + wave) * kWave + lane];
+  return rank;
+}
+
+// Survivors collected with an LDS counter, one key at a time.
+__device__ __forceinline__ void offer(uint64_t v, uint64_t T, uint64_t *cand,
+                                      uint32_t *cnt) {
+  if (v != 0ull && v >= T) {
+    const uint32_t pos = atomicAdd(cnt, 1u);
+    if (pos < (uint32_t)kCandCap) cand[pos] = v;
+  }
+}
+
+// Sorts cand[0, n) descending in place (n <= kCandCap) with a bitonic
+// network over the workgroup; only used when many keys tie above the bound.
+template <int WAVES>
+__device__ void block_sort_desc(uint64_t *cand, uint32_t n) {
+  constexpr int NT = WAVES * kWave;
+  uint32_t P = 2;
+  while (P < n) P <<= 1;
+  for (uint32_t i = n + threadIdx.x; i < P; i += NT) cand[i] = 0;
+  __syncthreads();
+  for (uint32_t size = 2; size <= P; size <<= 1) {
+    for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+      for (uint32_t i = threadIdx.x; i < P / 2; i += NT) {
+        const uint32_t lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
+        const uint64_t x = cand[lo], y = cand[hi];
+        if ((x < y) == ((lo & size) == 0)) {
+          cand[lo] = y;
+          cand[hi] = x;
+        }
       }
+      __syncthreads();
     }
   }
-  __builtin_amdgcn_wave_barrier();
-  return key;
 }
 
-// Rows a wave loads per step: VT_GEMV_ROWS, halved while the step's loads
-// plus h would need more than about 200 VGPRs ((U + MT) * CPL * 4).
+// Final merge for draft row m, run by the whole last workgroup after one
+// round of loads of the published tile partials:
+//   * softmax: global max of the tile maxima, then the sum of the tile sums
+//     rescaled to it, in a fixed order (no dependence on timing);
+//   * picks: the k-th largest key overall is at least T, the larger of the
+//     largest tile k-th key and the k-th largest of the 64 tile-group
+//     maxima (both are k-th largest keys of sets of real candidates; the
+//     tiles fold them in with atomic max). Keys >= T, typically a few
+//     dozen, are collected in LDS and ranked. With more than 64 survivors
+//     (exact ties, large k) a workgroup sort or, past kCandCap, k exact
+//     max rounds take over.
+template <int WAVES>
+__device__ void final_merge(const HeadArgs &a, int m, MergeShared<WAVES> &sh) {
+  constexpr int NT = WAVES * kWave;
+  const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
+  const int k = a.k, tiles = a.tiles;
+  const uint64_t *keys = a.tile_keys + (size_t)m * tiles * k;
+  const uint64_t *ms = a.tile_ms + (size_t)m * tiles;
+  uint64_t *gmax = a.group_max + (size_t)m * kGroups;
+  uint64_t *gkth = a.group_kth + (size_t)m * kGroups;
+  const int n = tiles * k;
+
+  // One round of loads: two batches of keys, the tile softmax partials and
+  // the group maxima.
+  constexpr int kBatch = 8;
+  uint64_t kb[2][kBatch];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int f = tid + (b * kBatch + j) * NT;
+      kb[b][j] = f < n ? fetch_u64(keys + f) : 0ull;
+    }
+  constexpr int kTpt = (kMaxTiles + NT - 1) / NT;  // tiles per thread
+  uint64_t mst[kTpt];
+#pragma unroll
+  for (int j = 0; j < kTpt; ++j) {
+    const int t = tid + j * NT;
+    mst[j] = t < tiles ? fetch_u64(ms + t) : 0ull;
+  }
+  uint64_t g = 0, gk = 0;
+  if (wave == 0) {
+    g = fetch_u64(gmax + lane);
+    gk = fetch_u64(gkth + lane);
+  }
+  float mu_l = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kTpt; ++j)
+    if (tid + j * NT < tiles) mu_l = fmaxf(mu_l, ms_max(mst[j]));
+  const float mu_w = wave_max(mu_l);
+  if (wave == 0) {
+    sh.sc[0][lane] = g;
+    sh.kmax = wave_max_u64(gk);
+  }
+  if (lane == 0) sh.f[wave] = mu_w;
+  if (tid == 0) sh.cnt = 0;
+  __syncthreads();
+  float mu = sh.f[0];
+  for (int w = 1; w < WAVES; ++w) mu = fmaxf(mu, sh.f[w]);
+  {
+    const uint32_t r = block_rank<WAVES, 1>(sh.sc[0], &sh.prank[0][0][0]);
+    if (wave == 0) {
+      const uint64_t hit = __ballot(r == (uint32_t)(k - 1) && g != 0ull);
+      if (lane == 0) sh.T = max_u64(hit ? readlane_u64(g, __builtin_ctzll(hit)) : 0ull, sh.kmax);
+    }
+  }
+  __syncthreads();  // all reads of sh.f done, T ready
+  if (wave == 0) {  // g and gk are in registers: reset the maxima for the next call
+    publish_u64(gmax + lane, 0ull);
+    publish_u64(gkth + lane, 0ull);
+  }
+  float s_l = 0.f;
+#pragma unroll
+  for (int j = 0; j < kTpt; ++j)
+    if (tid + j * NT < tiles) s_l += ms_sum(mst[j]) * __expf(ms_max(mst[j]) - mu);
+  const float s_w = wave_sum(s_l);
+  if (lane == 0) sh.f[wave] = s_w;
+  const uint64_t T = sh.T;
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) offer(kb[b][j], T, sh.cand, &sh.cnt);
+  for (int base = 2 * kBatch * NT; base < n; base += kBatch * NT) {
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int f = base + tid + j * NT;
+      kb[0][j] = f < n ? fetch_u64(keys + f) : 0ull;
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) offer(kb[0][j], T, sh.cand, &sh.cnt);
+  }
+  __syncthreads();
+  const uint32_t found = sh.cnt;
+  float S = sh.f[0];
+  for (int w = 1; w < WAVES; ++w) S += sh.f[w];
+  uint64_t key = 0;  // rank `tid` for tid < k
+  if (found <= (uint32_t)kWave) {
+    if (tid < kWave) {
+      sh.sc[0][tid] = tid < (int)found ? sh.cand[tid] : 0ull;
+      sh.sc[1][tid] = 0;
+    }
+    __syncthreads();
+    const uint32_t r = block_rank<WAVES, 1>(sh.sc[0], &sh.prank[0][0][0]);
+    if (wave == 0 && r < (uint32_t)k) sh.sc[1][r] = sh.sc[0][lane];
+    __syncthreads();
+    if (tid < kWave) key = sh.sc[1][tid];
+  } else if (found <= (uint32_t)kCandCap) {
+    block_sort_desc<WAVES>(sh.cand, found);
+    if (wave == 0) key = sh.cand[lane];
+  } else {
+    uint64_t prev = ~0ull;
+    for (int r = 0; r < k; ++r) {
+      uint64_t best = 0;
+      for (int f = tid; f < n; f += NT) {
+        const uint64_t v = fetch_u64(keys + f);
+        if (v < prev) best = max_u64(best, v);
+      }
+      best = wave_max_u64(best);
+      __syncthreads();
+      if (tid == 0) sh.kmax = 0;
+      __syncthreads();
+      if (lane == 0) atomicMax(&sh.kmax, (unsigned long long)best);
+      __syncthreads();
+      best = sh.kmax;
+      if (tid == r) key = best;
+      prev = best;
+    }
+  }
+  if (tid < k) {
+    a.full_ids[(size_t)m * k + tid] = key_id(key);
+    a.probs[(size_t)m * k + tid] = __expf(key_logit(key) - mu) / S;
+  }
+  __syncthreads();
+}
+
+// One row per wave and step: the W loads of a step (CPL 16-byte chunks per
+// lane) are all in flight at once, and 16 waves per workgroup keep enough
+// rows in flight per CU.
 template <int MT, int CPL>
-constexpr int rows_per_step() {
-  int u = VT_GEMV_ROWS;
-  while (u > 1 && (u + MT) * CPL > 50) u >>= 1;
-  return u;
+constexpr int rows_per_step() { return 1; }
+
+// Waves per workgroup: VT_GEMV_WAVES while h and one row fit the VGPRs
+// that many waves allow (128 at 16 waves), else 8.
+#ifndef VT_GEMV_WAVES
+#define VT_GEMV_WAVES 8
+#endif
+template <int MT, int CPL>
+constexpr int gemv_waves() {
+  return (VT_GEMV_WAVES <= 8 || (1 + MT) * CPL * 4 <= 96) ? VT_GEMV_WAVES : 8;
 }
 
-template <int MT, int CPL, bool RAGGED, bool LOGITS>
-__global__ __launch_bounds__(VT_GEMV_WAVES *kWave) void head_gemv_kernel(HeadArgs a) {
-  constexpr int WAVES = VT_GEMV_WAVES, U = rows_per_step<MT, CPL>();
+template <int WAVES, int MT, int CPL, bool RAGGED, bool LOGITS>
+__global__ __launch_bounds__(WAVES *kWave) void head_gemv_kernel(HeadArgs a) {
+  constexpr int U = rows_per_step<MT, CPL>();
   static_assert(kTileRows % (WAVES * U) == 0, "tile must split evenly");
   static_assert(MT <= WAVES, "one wave per draft row in the epilogue");
   __shared__ float s_z[MT][kTileRows];
-  __shared__ uint64_t s_buf[MT][kWave];
+  __shared__ MergeShared<WAVES> sh;
   __shared__ uint32_t s_slot;
 
   const int lane = __lane_id(), wave = threadIdx.x / kWave;
@@ -192,53 +360,37 @@ __global__ __launch_bounds__(VT_GEMV_WAVES *kWave) void head_gemv_kernel(HeadArg
 
   // Tile partial: top-k keys and softmax partial of each draft row.
   const int k = a.k;
+  const bool valid = row0 + lane < a.V_high;
+  uint64_t *s_key = sh.cand;               // [MT][64] keys of the tile
+  uint64_t *s_top = sh.cand + MT * kWave;  // [MT][64] ranked keys
   if (wave < MT) {
-    const int m = wave;
-    const bool valid = row0 + lane < a.V_high;
-    const float z = s_z[m][lane];
-    uint64_t key = valid ? make_key(z, fid) : 0ull;
-    key = wave_sort_desc(key);
-    const float mu = key_logit(readlane_u64(key, 0));
-    const float S = wave_sum(valid ? __expf(z - mu) : 0.f);
-    uint64_t *dst = a.tile_keys + ((size_t)m * a.tiles + tile) * k;
-    if (lane < k) dst[lane] = key;
-    if (lane == 0) a.tile_ms[(size_t)m * a.tiles + tile] = make_float2(mu, S);
+    s_key[wave * kWave + lane] = valid ? make_key(s_z[wave][lane], fid) : 0ull;
+    s_top[wave * kWave + lane] = 0;
   }
-
-  // Group merge by the group's last workgroup.
-  const int g = tile / a.group_size;
-  const int g_beg = g * a.group_size;
-  const int g_n = min(a.group_size, a.tiles - g_beg);
-  if (arrive(&a.counters[g], &s_slot) != (uint32_t)(g_n - 1)) return;
+  __syncthreads();
+  const uint32_t rank = block_rank<WAVES, MT>(s_key, &sh.prank[0][0][0]);
   if (wave < MT) {
     const int m = wave;
-    float mu, S;
-    const uint64_t key = merge_parts(
-        a.tile_keys + ((size_t)m * a.tiles + g_beg) * k,
-        a.tile_ms + (size_t)m * a.tiles + g_beg, g_n, k, s_buf[m], &mu, &S);
-    if (lane < k) a.group_keys[((size_t)m * a.groups + g) * k + lane] = key;
-    if (lane == 0) a.group_ms[(size_t)m * a.groups + g] = make_float2(mu, S);
-  }
-  if (threadIdx.x == 0)
-    __hip_atomic_store(&a.counters[g], 0u, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-
-  // Final merge by the last group merger: picks, probabilities, remap.
-  if (arrive(&a.counters[a.groups], &s_slot) != (uint32_t)(a.groups - 1)) return;
-  if (wave < MT) {
-    const int m = wave;
-    float mu, S;
-    const uint64_t key = merge_parts(a.group_keys + (size_t)m * a.groups * k,
-                                     a.group_ms + (size_t)m * a.groups,
-                                     a.groups, k, s_buf[m], &mu, &S);
-    if (lane < k) {
-      a.full_ids[(size_t)m * k + lane] = key_id(key);
-      a.probs[(size_t)m * k + lane] = __expf(key_logit(key) - mu) / S;
+    if (rank < (uint32_t)k) s_top[m * kWave + rank] = s_key[m * kWave + lane];
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t key = s_top[m * kWave + lane];
+    const float mu = key_logit(s_top[m * kWave]);
+    const float S = wave_sum(valid ? __expf(s_z[m][lane] - mu) : 0.f);
+    if (lane < k) publish_u64(a.tile_keys + ((size_t)m * a.tiles + tile) * k + lane, key);
+    if (lane == 0) {
+      publish_u64(a.tile_ms + (size_t)m * a.tiles + tile, pack_ms(mu, S));
+      const int grp = tile / a.tiles_per_group;
+      __hip_atomic_fetch_max(a.group_max + (size_t)m * kGroups + grp,
+                             s_top[m * kWave], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_max(a.group_kth + (size_t)m * kGroups + grp,
+                             s_top[m * kWave + k - 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  if (threadIdx.x == 0)
-    __hip_atomic_store(&a.counters[a.groups], 0u, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+
+  // The last tile to finish merges every tile's partial.
+  if (arrive(a.counter, &s_slot) != (uint32_t)(a.tiles - 1)) return;
+  for (int m = 0; m < MT; ++m) final_merge<WAVES>(a, m, sh);
+  if (threadIdx.x == 0) reset_counter(a.counter);
 }
 
 // ---------------------------------------------------------------- dispatch
@@ -246,8 +398,9 @@ constexpr int kCplSet[] = {1, 2, 3, 4, 5, 6, 7, 8, 12, 16};
 
 template <int MT, bool LOGITS, int CPL, bool RAGGED>
 hipError_t launch_one(const HeadArgs &a, hipStream_t stream) {
-  hipLaunchKernelGGL((head_gemv_kernel<MT, CPL, RAGGED, LOGITS>), dim3(a.tiles),
-                     dim3(VT_GEMV_WAVES * kWave), 0, stream, a);
+  constexpr int WAVES = gemv_waves<MT, CPL>();
+  hipLaunchKernelGGL((head_gemv_kernel<WAVES, MT, CPL, RAGGED, LOGITS>),
+                     dim3(a.tiles), dim3(WAVES * kWave), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -279,23 +432,18 @@ hipError_t launch_gemv(const HeadArgs &a, hipStream_t stream) {
 }  // namespace
 
 HeadPlan head_plan(int32_t M, int32_t V_high, int32_t k) {
+  // Fixed-offset prefix that every call leaves at zero: the ticket counter,
+  // then the group maxima of up to VT_M_MAX draft rows. Per-call data after.
   HeadPlan p;
   p.tiles = (V_high + kTileRows - 1) / kTileRows;
-  int gs = 1;
-  while (gs * gs < p.tiles) ++gs;
-  if (gs > 64) gs = 64;
-  if ((p.tiles + gs - 1) / gs > 64) gs = (p.tiles + 63) / 64;
-  p.group_size = gs;
-  p.groups = (p.tiles + gs - 1) / gs;
-  size_t off = align_up((size_t)(p.groups + 1) * 4, 256);
+  size_t off = 256;
+  p.off_group = off;
+  off += (size_t)VT_M_MAX * 2 * kGroups * 8;
+  p.zero_bytes = off;
   p.off_tile_keys = off;
   off += align_up((size_t)M * p.tiles * k * 8, 256);
   p.off_tile_ms = off;
   off += align_up((size_t)M * p.tiles * 8, 256);
-  p.off_group_keys = off;
-  off += align_up((size_t)M * p.groups * k * 8, 256);
-  p.off_group_ms = off;
-  off += align_up((size_t)M * p.groups * 8, 256);
   p.bytes = off;
   return p;
 }
@@ -313,13 +461,12 @@ hipError_t launch_draft_head(const uint16_t *h, int32_t M, int32_t d,
   a.V_high = V_high;
   a.k = k;
   a.tiles = p.tiles;
-  a.group_size = p.group_size;
-  a.groups = p.groups;
-  a.counters = reinterpret_cast<uint32_t *>(base);
+  a.counter = reinterpret_cast<uint32_t *>(base);
   a.tile_keys = reinterpret_cast<uint64_t *>(base + p.off_tile_keys);
-  a.tile_ms = reinterpret_cast<float2 *>(base + p.off_tile_ms);
-  a.group_keys = reinterpret_cast<uint64_t *>(base + p.off_group_keys);
-  a.group_ms = reinterpret_cast<float2 *>(base + p.off_group_ms);
+  a.tile_ms = reinterpret_cast<uint64_t *>(base + p.off_tile_ms);
+  a.group_max = reinterpret_cast<uint64_t *>(base + p.off_group);
+  a.group_kth = a.group_max + (size_t)VT_M_MAX * kGroups;
+  a.tiles_per_group = (p.tiles + kGroups - 1) / kGroups;
   // Up to 4 draft rows per pass over W_trim.
   for (int32_t m0 = 0; m0 < M; m0 += 4) {
     HeadArgs c = a;

@@ -1,6 +1,6 @@
 // Device helpers shared by the gfx950 kernels: wave64 reductions on DPP,
-// order-preserving 64-bit top-k keys, bitonic sort across a wave, and
-// cross-workgroup release/acquire.
+// order-preserving 64-bit top-k keys, bitonic sort across a wave, and the
+// hand-off of partial results between workgroups.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -155,21 +155,43 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key) {
 }
 
 // -------------------------------------------------- cross-workgroup order
-// Publishes this workgroup's global writes and takes a ticket: returns the
-// number of workgroups that arrived before it. Must be called by every
-// thread of the workgroup (it contains a barrier); the return value is
-// uniform.
+// Workgroups hand partial results to the last one to finish without any
+// cache-wide maintenance. On gfx950 each XCD has its own L2; an agent-scope
+// release/acquire would write back (buffer_wbl2) and invalidate (buffer_inv)
+// a whole L2 in every workgroup, which costs far more than the data moved
+// here. Instead every value that crosses workgroups is written and read
+// with agent-scope atomic stores and loads (global_store/load ... sc1),
+// which are coherent across XCDs by themselves:
+//   writer: publish_u64() stores, then arrive(): s_waitcnt vmcnt(0) makes
+//           this wave's sc1 stores complete, the barrier extends that to
+//           the workgroup, then one relaxed agent-scope atomic add takes a
+//           ticket;
+//   reader: the workgroup that draws the last ticket reads the data with
+//           fetch_u64(); its loads are issued only after the ticket returns.
+// Nothing else may be used to pass data between workgroups.
+__device__ __forceinline__ void publish_u64(uint64_t *p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t fetch_u64(const uint64_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Takes a ticket after this workgroup's published stores have completed;
+// returns how many workgroups arrived before it. Every thread of the
+// workgroup must call it (it contains barriers); the result is uniform.
 __device__ __forceinline__ uint32_t arrive(uint32_t *counter, uint32_t *s_slot) {
-  __threadfence();
+  __builtin_amdgcn_s_waitcnt(0);  // vmcnt/lgkmcnt/expcnt = 0: stores done
   __syncthreads();
-  if (threadIdx.x == 0) {
-    *s_slot = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL,
+  if (threadIdx.x == 0)
+    *s_slot = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
-  }
   __syncthreads();
-  const uint32_t t = *s_slot;
-  __threadfence();  // acquire side: see what the earlier arrivals published
-  return t;
+  return *s_slot;
+}
+
+// Returns a ticket counter to zero for the next call (by its last holder).
+__device__ __forceinline__ void reset_counter(uint32_t *counter) {
+  __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace vt

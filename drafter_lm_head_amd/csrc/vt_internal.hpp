@@ -35,12 +35,12 @@ hipError_t launch_gather(const uint16_t *W, int32_t V, int32_t d,
                          const int32_t *t2f, int32_t V_high, uint16_t *W_trim,
                          uint32_t *n_bad, hipStream_t stream);
 
-// Draft head: tiles of kTileRows rows of W_trim; tile partials are merged
-// in groups, then the group results are merged once.
+// Draft head: tiles of kTileRows rows of W_trim; the last tile to finish
+// merges every tile's partial result.
 constexpr int kTileRows = 64;
 struct HeadPlan {
-  int32_t tiles, group_size, groups;
-  size_t off_tile_keys, off_tile_ms, off_group_keys, off_group_ms;
+  int32_t tiles;
+  size_t off_group, zero_bytes, off_tile_keys, off_tile_ms;
   size_t bytes;
 };
 HeadPlan head_plan(int32_t M, int32_t V_high, int32_t k);
