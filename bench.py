@@ -10,11 +10,12 @@ seeded Zipf ids, select, gather), which is timed too and reported under
 Inputs are resident in HBM before timing starts. W_trim (256 MiB) is about
 the size of the 256 MB Infinity Cache, so timed calls rotate over copies
 totalling at least 1 GiB ("cold", the reported value); a single resident
-copy is reported as "warm". The roofline object uses per-launch HIP events
-on the stream the kernel runs on.
+copy is reported as "warm". The roofline object divides the algorithmic
+bytes of one call by the average call time over the timed region, taken
+with HIP events on the stream the kernel runs on.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--M M] [--sweep] [--no-cpu]
+                       [--M M] [--sweep] [--no-cpu] [--only-head] [--calib-copy]
 """
 from __future__ import annotations
 
@@ -76,6 +77,26 @@ def median_us(fn, reps, torch):
     return statistics.median(ts)
 
 
+def recorded_traffic():
+    """HBM bytes per launch of the head kernel from the committed counter
+    summary, or None if the kernel sources changed since it was taken."""
+    import hashlib
+    prof = os.path.join(ROOT, "profiles", "head_gemv_llama3_8b_m1.md")
+    if not os.path.exists(prof):
+        return None
+    fields = {}
+    for line in open(prof):
+        if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "source_sha256"):
+            key, val = line.split(":", 1)
+            fields[key] = val.strip()
+    h = hashlib.sha256()
+    for f in ("head.hip", "vt_device.hpp", "vt_internal.hpp"):
+        h.update(open(os.path.join(ROOT, "drafter_lm_head_amd", "csrc", f), "rb").read())
+    if fields.get("source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(h, Wt, t2f, k, budget_s=12.0):
     import oracle
     oracle.draft_head(h[:1], Wt[:64], t2f[:64], 1)      # load + page in
@@ -100,6 +121,10 @@ def main():
     ap.add_argument("--M", type=int, default=None)
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only-head", action="store_true",
+                    help="time only the cold draft-head steps (for profiler runs)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the draft head is measured on one "
@@ -133,7 +158,7 @@ def main():
     Wt = dlh.vt_gather_head(W, t2f)
     torch.cuda.synchronize()
     cov = dlh.coverage(sel, tot)
-    reps = 7
+    reps = 1 if args.only_head else 7
     us_count = median_us(lambda: dlh.vt_count_freq(ids, w.V, counts=counts, n_invalid=n_inv), reps, torch)
     us_select = median_us(lambda: dlh.vt_select_vocab(counts, w.V_high), reps, torch)
     us_gather = median_us(lambda: dlh.vt_gather_head(W, t2f, out=Wt), reps, torch)
@@ -164,12 +189,27 @@ def main():
     ms_step = ms_total / args.steps
     value = 1000.0 / ms_step
     nb = head_bytes(V_high, d, M, k)
+    # Roofline: algorithmic bytes over the kernel's average duration in the
+    # timed region (events on the stream the kernel runs on).
+    achieved = nb / (ms_step * 1e-3) / 1e9
+    log(f"cold: {ms_step * 1000:.2f} us/step, {achieved:.0f} GB/s")
+    if args.calib_copy:
+        src = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 10 x 256 MiB")
+        del src, dst
+    if args.only_head:
+        print(json.dumps({"metric": METRIC, "value": round(value, 1), "unit": "calls/s",
+                          "ms_per_step": round(ms_step, 6), "steps": args.steps,
+                          "GB_per_s": round(achieved, 1)}), flush=True)
+        return
     n_launch = min(args.steps, 1000)
-    us_kernel = per_launch_us(cold, n_launch, torch)
-    achieved = nb / (us_kernel * 1e-6) / 1e9
-    log(f"cold: {ms_step * 1000:.2f} us/step, per-launch {us_kernel:.2f} us, {achieved:.0f} GB/s")
+    us_launch = per_launch_us(cold, n_launch, torch)
     ms_warm = time_calls(warm, args.steps, torch) / args.steps
-    log(f"warm: {ms_warm * 1000:.2f} us/step")
+    log(f"warm: {ms_warm * 1000:.2f} us/step; single launches bracketed by events: {us_launch:.2f} us")
 
     # pipeline: one pass of every step (count, select, gather, draft head)
     def pipeline():
@@ -235,9 +275,11 @@ def main():
         "us_per_call": round(ms_step * 1000, 3),
         "hbm_frac": round(nb / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic() if (w.name == "llama3_8b" and M == 1) else None,
                      "kernel": "head_gemv_kernel", "bytes_per_launch": nb,
-                     "us_per_launch": round(us_kernel, 3)},
+                     "us_per_launch": round(ms_step * 1000, 3),
+                     "us_single_launch_events": round(us_launch, 3)},
         "cpu_baseline": cpu,
         "warm": {"us_per_call": round(ms_warm * 1000, 3),
                  "GB_per_s": round(nb / (ms_warm * 1e-3) / 1e9, 1)},
