@@ -23,6 +23,7 @@ namespace vt {
 namespace {
 
 constexpr int kGroups = 64;  // tile groups whose maxima bound the k-th key
+constexpr int kGemvMaxRows = 4;  // up to this many draft rows: GEMV path
 
 struct HeadArgs {
   const u32x4 *h;        // [M, c16]
@@ -39,6 +40,7 @@ struct HeadArgs {
   int32_t *full_ids;     // [M][k]
   float *probs;          // [M][k]
   float *logits;         // [M][V_high], logits-only variant
+  const u32x4 *hp;       // h in MFMA B-operand order (MFMA path)
 };
 
 __device__ __forceinline__ uint64_t pack_ms(float mu, float S) {
@@ -393,6 +395,198 @@ __global__ __launch_bounds__(WAVES *kWave) void head_gemv_kernel(HeadArgs a) {
   if (threadIdx.x == 0) reset_counter(a.counter);
 }
 
+// ---------------------------------------------------------------- MFMA path
+// Draft trees (M = 5..64 rows): the head is a skinny GEMM, z^T = W_trim h^T.
+// v_mfma_f32_16x16x32_bf16 takes 16 W rows as the A operand and 16 draft rows
+// as the B operand; lane l supplies 16 bytes (8 k-values) of row l % 16 at
+// k-chunk 4 s + l / 16 of k-step s, the same chunk for A and B, and receives
+// C[4 (l / 16) + r][l % 16] in accumulator register r. A workgroup owns a
+// tile of 64 W rows; its 4 waves split d into contiguous k ranges, stream
+// their slices of W once (16 KiB per wave in flight) and read h from L2. The partial products are summed over the waves in a fixed order
+// in LDS; each draft row's tile partial is then published exactly as on the
+// GEMV path, and a second kernel merges one draft row per workgroup.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMfmaWaves = 4;
+
+// One wave publishes one draft row's tile partial: lane j holds the key of
+// tile row j (0 past V_high) and its logit z. The tile's top-k come from
+// rank counting over LDS broadcasts; sc and top are 64-key LDS buffers of
+// this wave (16-byte aligned).
+__device__ __forceinline__ void wave_publish_tile(const HeadArgs &a, int m, int tile,
+                                                  uint64_t key, float z, bool valid,
+                                                  uint64_t *sc, uint64_t *top) {
+  typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+  const int lane = __lane_id(), k = a.k;
+  sc[lane] = key;
+  top[lane] = 0;
+  __builtin_amdgcn_wave_barrier();
+  uint32_t rank = 0;
+#pragma unroll
+  for (int j = 0; j < kWave; j += 2) {
+    const u64x2 q = *reinterpret_cast<const u64x2 *>(sc + j);
+    rank += q.x > key;
+    rank += q.y > key;
+  }
+  if (rank < (uint32_t)k) top[rank] = key;
+  __builtin_amdgcn_wave_barrier();
+  const uint64_t tk = top[lane];
+  const uint64_t head = top[0], kth = top[k - 1];
+  const float mu = key_logit(head);
+  const float S = wave_sum(valid ? __expf(z - mu) : 0.f);
+  if (lane < k) publish_u64(a.tile_keys + ((size_t)m * a.tiles + tile) * k + lane, tk);
+  if (lane == 0) {
+    publish_u64(a.tile_ms + (size_t)m * a.tiles + tile, pack_ms(mu, S));
+    const int grp = tile / a.tiles_per_group;
+    __hip_atomic_fetch_max(a.group_max + (size_t)m * kGroups + grp, head,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_max(a.group_kth + (size_t)m * kGroups + grp, kth,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// W is staged through wave-private LDS: the operand layout (16 rows x 64
+// bytes per load) is slow to fetch from HBM directly, so each load
+// instruction instead reads 4 rows x 256 contiguous bytes; rows are padded
+// by 16 bytes in LDS so that the operand reads are free of bank conflicts.
+constexpr int kStageChunks = 16;                      // 16-byte chunks per row and stage
+constexpr int kStagePitch = kStageChunks + 1;         // row pitch in chunks
+constexpr int kStageSize = kTileRows * kStagePitch;   // chunks per wave
+
+// h re-laid out in B-operand order, so that each B load of the MFMA loop
+// reads 1 KiB contiguous: hp[(s * NT + cb) * 64 + l] = the 16-byte chunk
+// 4 s + l / 16 of draft row 16 cb + l % 16 (zero past M or d).
+__global__ __launch_bounds__(kWave) void h_pack_kernel(const u32x4 *__restrict__ h, int M,
+                                                       int c16, int NT, u32x4 *__restrict__ hp) {
+  const int s = blockIdx.x / NT, cb = blockIdx.x % NT, l = threadIdx.x;
+  const int row = cb * 16 + (l & 15), ch = 4 * s + (l >> 4);
+  hp[(size_t)blockIdx.x * kWave + l] =
+      (row < M && ch < c16) ? h[(size_t)row * c16 + ch] : u32x4{0, 0, 0, 0};
+}
+
+template <int NT>
+__global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a) {
+  union alignas(16) Smem {
+    u32x4 stage[kMfmaWaves][kStageSize];
+    float part[kMfmaWaves][NT * 16][kTileRows];
+  };
+  __shared__ Smem sm;
+  __shared__ alignas(16) uint64_t s_sc[kMfmaWaves][2][kWave];
+  const int lane = __lane_id(), wave = threadIdx.x / kWave;
+  const int tile = blockIdx.x, row0 = tile * kTileRows;
+  const int c16 = a.c16, M = a.M;
+  const int g = lane >> 4, r16 = lane & 15;
+  // This wave's contiguous range of 16-byte chunks (a multiple of 4).
+  const int cq = ((c16 + kMfmaWaves - 1) / kMfmaWaves + 3) / 4 * 4;
+  const int c_lo = min(c16, wave * cq), c_hi = min(c16, c_lo + cq);
+
+  // Uniform bases plus 32-bit per-lane offsets (in 16-byte chunks).
+  const u32x4 *tileW = a.W + (size_t)row0 * c16;
+  const int last_row = a.V_high - 1 - row0;  // rows past V_high re-read this one
+  u32x4 *st = sm.stage[wave];
+
+  f32x4 acc[4][NT];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < NT; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 v[kStageChunks];
+  // Stage loads: instruction q covers tile rows 4q .. 4q + 3, 256 bytes each.
+  auto load_stage = [&](int base) {
+    const int ch = base + r16;
+#pragma unroll
+    for (int q = 0; q < kStageChunks; ++q)
+      v[q] = ch < c_hi ? load_stream16(tileW + min(4 * q + g, last_row) * c16 + ch)
+                       : u32x4{0, 0, 0, 0};
+  };
+  if (c_lo < c_hi) load_stage(c_lo);
+#pragma unroll 1
+  for (int base = c_lo; base < c_hi; base += kStageChunks) {
+#pragma unroll
+    for (int q = 0; q < kStageChunks; ++q) st[(4 * q + g) * kStagePitch + r16] = v[q];
+    __builtin_amdgcn_wave_barrier();
+    if (base + kStageChunks < c_hi) load_stage(base + kStageChunks);
+    // B operands of the whole stage (contiguous loads from L2), then per
+    // k-step the A operands from LDS and the MFMAs; the barriers keep the
+    // compiler from hoisting every A read (register pressure).
+    u32x4 bv[kStageChunks / 4][NT];
+#pragma unroll
+    for (int t = 0; t < kStageChunks / 4; ++t) {
+      const bool ok = base + 4 * t + g < c_hi;
+      const u32x4 *hs = a.hp + (size_t)((base / 4 + t) * NT) * kWave + lane;
+#pragma unroll
+      for (int cb = 0; cb < NT; ++cb) bv[t][cb] = ok ? hs[cb * kWave] : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int t = 0; t < kStageChunks / 4; ++t) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int cl = 4 * t + g;  // chunk within the stage for this lane
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const u32x4 av = st[(rb * 16 + r16) * kStagePitch + cl];
+#pragma unroll
+        for (int cb = 0; cb < NT; ++cb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv[t][cb]), acc[rb][cb],
+              0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();  // every wave is done with its stage before part[] reuses it
+
+  // Partial products to LDS as [draft row][tile row], then a fixed-order sum
+  // over the waves into wave 0's slot.
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < NT; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.part[wave][cb * 16 + r16][rb * 16 + 4 * g + r] = acc[rb][cb][r];
+  __syncthreads();
+  float *z0 = &sm.part[0][0][0];
+  for (int i = threadIdx.x; i < NT * 16 * kTileRows; i += kMfmaWaves * kWave) {
+    float val = z0[i];
+#pragma unroll
+    for (int w = 1; w < kMfmaWaves; ++w) val += (&sm.part[w][0][0])[i];
+    z0[i] = val;
+  }
+  __syncthreads();
+
+  const bool valid = row0 + lane < a.V_high;
+  const int32_t fid = valid ? a.t2f[row0 + lane] : 0;
+  for (int m = wave; m < M; m += kMfmaWaves) {
+    const float z = sm.part[0][m][lane];
+    wave_publish_tile(a, m, tile, valid ? make_key(z, fid) : 0ull, z, valid,
+                      s_sc[wave][0], s_sc[wave][1]);
+  }
+}
+
+// One workgroup per draft row merges the published tile partials.
+template <int WAVES>
+__global__ __launch_bounds__(WAVES *kWave) void head_merge_kernel(HeadArgs a) {
+  __shared__ MergeShared<WAVES> sh;
+  final_merge<WAVES>(a, blockIdx.x, sh);
+}
+
+template <int NT>
+hipError_t launch_mfma(const HeadArgs &a, hipStream_t stream) {
+  const int steps = (a.c16 + 3) / 4;
+  hipLaunchKernelGGL(h_pack_kernel, dim3(steps * NT), dim3(kWave), 0, stream, a.h, a.M,
+                     a.c16, NT, const_cast<u32x4 *>(a.hp));
+  hipError_t e0 = hipGetLastError();
+  if (e0 != hipSuccess) return e0;
+  hipLaunchKernelGGL((head_mfma_kernel<NT>), dim3(a.tiles), dim3(kMfmaWaves * kWave), 0,
+                     stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((head_merge_kernel<8>), dim3(a.M), dim3(8 * kWave), 0, stream, a);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- dispatch
 constexpr int kCplSet[] = {1, 2, 3, 4, 5, 6, 7, 8, 12, 16};
 
@@ -444,6 +638,8 @@ HeadPlan head_plan(int32_t M, int32_t V_high, int32_t k) {
   off += align_up((size_t)M * p.tiles * k * 8, 256);
   p.off_tile_ms = off;
   off += align_up((size_t)M * p.tiles * 8, 256);
+  p.off_hpack = off;  // MFMA path: h in B-operand order, 16 * NT rows x d
+  off += M > kGemvMaxRows ? align_up((size_t)((M + 15) / 16) * 16 * (size_t)VT_D_MAX * 2, 256) : 0;
   p.bytes = off;
   return p;
 }
@@ -467,17 +663,20 @@ hipError_t launch_draft_head(const uint16_t *h, int32_t M, int32_t d,
   a.group_max = reinterpret_cast<uint64_t *>(base + p.off_group);
   a.group_kth = a.group_max + (size_t)VT_M_MAX * kGroups;
   a.tiles_per_group = (p.tiles + kGroups - 1) / kGroups;
-  // Up to 4 draft rows per pass over W_trim.
-  for (int32_t m0 = 0; m0 < M; m0 += 4) {
-    HeadArgs c = a;
-    c.M = min(4, M - m0);
-    c.h = reinterpret_cast<const u32x4 *>(h + (size_t)m0 * d);
-    c.full_ids = full_ids + (size_t)m0 * k;
-    c.probs = probs + (size_t)m0 * k;
-    hipError_t e = launch_gemv(c, stream);
-    if (e != hipSuccess) return e;
+  a.hp = reinterpret_cast<const u32x4 *>(base + p.off_hpack);
+  a.M = M;
+  a.h = reinterpret_cast<const u32x4 *>(h);
+  a.full_ids = full_ids;
+  a.probs = probs;
+  // Up to kGemvMaxRows rows: one GEMV pass with the merge in the same
+  // kernel. More rows: the MFMA skinny GEMM, then one merge workgroup per row.
+  if (M <= kGemvMaxRows) return launch_gemv(a, stream);
+  switch ((M + 15) / 16) {
+    case 1: return launch_mfma<1>(a, stream);
+    case 2: return launch_mfma<2>(a, stream);
+    case 3: return launch_mfma<3>(a, stream);
+    default: return launch_mfma<4>(a, stream);
   }
-  return hipSuccess;
 }
 
 hipError_t launch_head_logits(const uint16_t *h, int32_t M, int32_t d,

@@ -61,6 +61,19 @@ def test_draft_rows(dlh, M):
     check_case(dlh, h, W, t2f, 10)
 
 
+@pytest.mark.parametrize("M", [17, 33, 60, 64])
+def test_draft_tree_rows(dlh, M):
+    # M > 4 runs the MFMA skinny GEMM and one merge workgroup per row.
+    h, W, t2f = rand_case(200 + M, M, 1024, 2500)
+    check_case(dlh, h, W, t2f, 10)
+
+
+@pytest.mark.parametrize("V_high,d,k", [(1, 256, 1), (70, 520, 10), (129, 8, 64), (3000, 3584, 64)])
+def test_draft_tree_edges(dlh, V_high, d, k):
+    h, W, t2f = rand_case(300 + V_high, 60, d, V_high, hscale=2.0)
+    check_case(dlh, h, W, t2f, min(k, V_high))
+
+
 @pytest.mark.parametrize("V_high", [1, 10, 63, 64, 65, 1000, 4097])
 def test_ragged_vocab(dlh, V_high):
     h, W, t2f = rand_case(V_high, 2, 256, V_high)
@@ -169,6 +182,23 @@ def test_llama_head_full_size(dlh, llama, M, scale):
     h = synth.make_hidden(w, M=M, scale=scale)
     worst = check_case(dlh, h, Wt, t2f, w.k)
     print("worst", worst)
+
+
+def test_eagle2_tree_full_size(dlh, llama):
+    # EAGLE-2-style draft tree: 60 rows per step on the LLaMA-3-8B head.
+    w, Wt, t2f = llama
+    h = synth.make_hidden(w, M=60)
+    print("worst", check_case(dlh, h, Wt, t2f, w.k))
+
+
+@pytest.mark.parametrize("M", [16, 64])
+def test_qwen_head_full_size(dlh, M):
+    w = synth.WORKLOADS["qwen2_7b"]
+    rng = np.random.default_rng(77)
+    Wt = synth.bf16_bits_from_f32(rng.standard_normal((w.V_high, w.d), dtype=np.float32) * np.float32(0.02))
+    t2f = rng.permutation(w.V)[: w.V_high].astype(np.int32)
+    h = synth.make_hidden(w, M=M)
+    print("worst", check_case(dlh, h, Wt, t2f, w.k))
 
 
 def test_llama_logits_bound(dlh, llama):
