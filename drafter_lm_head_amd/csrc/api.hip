@@ -74,6 +74,7 @@ int vt_select_vocab(const uint32_t *counts, int32_t V, int32_t V_high,
                     uint64_t *tot_sum, void *ws, size_t ws_bytes,
                     void *stream) {
   if (!counts || !t2f || !sel_sum || !tot_sum) return VT_ERR_INVALID_ARG;
+  if (!aligned(counts, 16)) return VT_ERR_INVALID_ARG;
   if (V <= 0 || V_high <= 0 || V_high > V) return VT_ERR_INVALID_ARG;
   if (!ws || !aligned(ws, 256) ||
       ws_bytes < vt_select_vocab_workspace_size(V, V_high))

@@ -6,13 +6,17 @@
 // (at most 608 KB) stay in L2, so one workgroup of 1024 threads does the
 // whole selection in one launch:
 //   1. radix select (11/11/10-bit digits) of the V_high-th largest count c*,
-//      and `need`, the number of ids with count c* that are kept;
+//      and `need`, the number of ids with count c* that are kept; the first
+//      pass also sums all counts and finds the largest;
 //   2. stable compaction, in id order, of the ids with count > c* and the
 //      first `need` ids with count == c*;
 //   3. stable LSD radix sort (8-bit digits) of the kept (count, id) pairs by
 //      descending count, over only the bits the largest count uses; since the
 //      pairs start in id order, equal counts stay in ascending id order;
 //   4. t2f, f2t and the two sums.
+// Counts of a frequency histogram are very skewed (most ids share a few
+// small values), so digit histograms combine each wave's most common digit
+// into one LDS atomic; loads are 16 bytes wide with several in flight.
 #include "vt_internal.hpp"
 
 namespace vt {
@@ -21,6 +25,7 @@ namespace {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kUnroll = 8;  // 16-byte loads in flight per thread
 
 struct SelShared {
   uint32_t hist[2048];
@@ -75,6 +80,54 @@ __device__ uint32_t block_max_u32(uint32_t x, SelShared &s) {
   return t;
 }
 
+// counts[4 i .. 4 i + 3] with entries past V read as 0 and never loaded
+// (counts is 16-byte aligned; only the last, partial vector uses scalars).
+__device__ __forceinline__ u32x4 load_counts4(const uint32_t *counts, int32_t V, int32_t i) {
+  if (4 * i + 3 < V) return reinterpret_cast<const u32x4 *>(counts)[i];
+  u32x4 q = {0, 0, 0, 0};
+  if (4 * i + 0 < V) q.x = counts[4 * i + 0];
+  if (4 * i + 1 < V) q.y = counts[4 * i + 1];
+  if (4 * i + 2 < V) q.z = counts[4 * i + 2];
+  return q;
+}
+
+// hist[d] += 1 for every active lane. The lanes that share the first active
+// lane's digit add with one atomic; the others add one by one. Every lane of
+// the wave must call it.
+__device__ __forceinline__ void hist_add(uint32_t *hist, uint32_t d, bool active) {
+  const uint64_t act = __ballot(active);
+  if (act == 0) return;
+  const int leader = (int)__builtin_ctzll(act);
+  const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)d, leader);
+  const uint64_t same = __ballot(active && d == d0);
+  if (__lane_id() == leader) atomicAdd(&hist[d0], (uint32_t)__popcll(same));
+  if (active && d != d0) atomicAdd(&hist[d], 1u);
+}
+
+// Calls f(v, c) for every id v < V (coalesced 16-byte loads, kUnroll in
+// flight); the loop trip count is uniform so f may use wave-wide ops, and
+// ids past V are passed with valid = false.
+template <typename F>
+__device__ __forceinline__ void for_counts(const uint32_t *counts, int32_t V, F f) {
+  const int32_t n4 = (V + 3) / 4;
+  for (int32_t base = 0; base < n4; base += kUnroll * kSelThreads) {
+    u32x4 q[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int32_t i = base + u * kSelThreads + (int)threadIdx.x;
+      q[u] = i < n4 ? load_counts4(counts, V, i) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int32_t v = 4 * (base + u * kSelThreads + (int)threadIdx.x);
+      f(v + 0, q[u].x, v + 0 < V);
+      f(v + 1, q[u].y, v + 1 < V);
+      f(v + 2, q[u].z, v + 2 < V);
+      f(v + 3, q[u].w, v + 3 < V);
+    }
+  }
+}
+
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const uint32_t *__restrict__ counts, int32_t V, int32_t V_high,
     int32_t *__restrict__ t2f, int32_t *__restrict__ f2t,
@@ -83,18 +136,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   __shared__ SelShared s;
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
 
-  // ---- 0. total and largest count
+  // ---- 1. radix select of c*, the V_high-th largest count (the first pass
+  // also totals the counts and finds the largest)
   unsigned long long tot = 0;
   uint32_t cmax = 0;
-  for (int32_t v = tid; v < V; v += kSelThreads) {
-    const uint32_t c = counts[v];
-    tot += c;
-    cmax = max(cmax, c);
-  }
-  tot = block_sum_u64(tot, s);
-  cmax = block_max_u32(cmax, s);
-
-  // ---- 1. radix select of c*, the V_high-th largest count
   uint32_t prefix = 0, pmask = 0, need = (uint32_t)V_high;
   const int shifts[3] = {21, 10, 0}, widths[3] = {11, 11, 10};
   for (int p = 0; p < 3; ++p) {
@@ -102,10 +147,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const uint32_t nd = 1u << widths[p], dm = nd - 1;
     for (uint32_t i = tid; i < nd; i += kSelThreads) s.hist[i] = 0;
     __syncthreads();
-    for (int32_t v = tid; v < V; v += kSelThreads) {
-      const uint32_t c = counts[v];
-      if ((c & pmask) == prefix) atomicAdd(&s.hist[(c >> sh) & dm], 1u);
-    }
+    for_counts(counts, V, [&](int32_t, uint32_t c, bool valid) {
+      if (p == 0 && valid) {
+        tot += c;
+        cmax = max(cmax, c);
+      }
+      hist_add(s.hist, (c >> sh) & dm, valid && (c & pmask) == prefix);
+    });
     __syncthreads();
     // Thread t owns digits d0 = nd-1-2t and d1 = d0-1 (largest first).
     const int d0 = (int)nd - 1 - 2 * tid, d1 = d0 - 1;
@@ -125,16 +173,30 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     need = s.need;
     __syncthreads();
   }
+  tot = block_sum_u64(tot, s);
+  cmax = block_max_u32(cmax, s);
   const uint32_t cstar = prefix;  // ids with count > c* all kept; `need` ties kept
 
-  // ---- 2. stable compaction in id order
-  const int32_t run = (V + kSelThreads - 1) / kSelThreads;
-  const int32_t vb = min(V, tid * run), ve = min(V, vb + run);
+  // ---- 2. stable compaction in id order: thread t owns the ids of a
+  // contiguous run of 16-byte vectors.
+  const int32_t n4 = (V + 3) / 4;
+  const int32_t run4 = (n4 + kSelThreads - 1) / kSelThreads;
+  const int32_t i4b = min(n4, tid * run4), i4e = min(n4, i4b + run4);
   uint32_t n_gt = 0, n_eq = 0;
-  for (int32_t v = vb; v < ve; ++v) {
-    const uint32_t c = counts[v];
-    n_gt += c > cstar;
-    n_eq += c == cstar;
+  for (int32_t i4 = i4b; i4 < i4e; i4 += kUnroll) {
+    u32x4 q[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) q[u] = i4 + u < i4e ? load_counts4(counts, V, i4 + u) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t cc[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool valid = i4 + u < i4e && 4 * (i4 + u) + e < V;
+        n_gt += valid && cc[e] > cstar;
+        n_eq += valid && cc[e] == cstar;
+      }
+    }
   }
   uint32_t scan_total;
   const uint32_t eq_before = block_excl_scan(n_eq, s, &scan_total);
@@ -143,12 +205,24 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   uint32_t pos = block_excl_scan(n_gt + eq_take, s, &scan_total);
   {
     uint32_t eq_rank = eq_before;
-    for (int32_t v = vb; v < ve; ++v) {
-      const uint32_t c = counts[v];
-      bool keep = c > cstar;
-      if (c == cstar) keep = eq_rank++ < need;
-      // pos < V_high always holds; the test keeps a logic error in bounds
-      if (keep && pos < (uint32_t)V_high) bufA[pos++] = ((uint64_t)c << 32) | (uint32_t)v;
+    for (int32_t i4 = i4b; i4 < i4e; i4 += kUnroll) {
+      u32x4 q[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) q[u] = i4 + u < i4e ? load_counts4(counts, V, i4 + u) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const uint32_t cc[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int32_t v = 4 * (i4 + u) + e;
+          if (i4 + u >= i4e || v >= V) continue;
+          const uint32_t c = cc[e];
+          bool keep = c > cstar;
+          if (c == cstar) keep = eq_rank++ < need;
+          // pos < V_high always holds; the test keeps a logic error in bounds
+          if (keep && pos < (uint32_t)V_high) bufA[pos++] = ((uint64_t)c << 32) | (uint32_t)v;
+        }
+      }
     }
   }
   __threadfence_block();
@@ -167,9 +241,19 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       s.drun[i] = 0;
     }
     __syncthreads();
-    for (int32_t i = tid; i < V_high; i += kSelThreads) {
-      const uint32_t key = (~(uint32_t)(src[i] >> 32)) & kmask;
-      atomicAdd(&s.hist[(key >> sh) & 255u], 1u);
+    for (int32_t base = 0; base < V_high; base += kUnroll * kSelThreads) {
+      uint64_t e[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int32_t i = base + u * kSelThreads + tid;
+        e[u] = i < V_high ? src[i] : 0ull;
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int32_t i = base + u * kSelThreads + tid;
+        const uint32_t key = (~(uint32_t)(e[u] >> 32)) & kmask;
+        hist_add(s.hist, (key >> sh) & 255u, i < V_high);
+      }
     }
     __syncthreads();
     if (wave == 0) {  // exclusive scan of the 256 digit counts
@@ -186,15 +270,15 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       }
     }
     __syncthreads();
+    // Tiles of 1024 elements in order; the next tile's element is loaded
+    // while this one is ranked.
+    uint64_t e_next = tid < V_high ? src[tid] : 0ull;
     for (int32_t base = 0; base < V_high; base += kSelThreads) {
       const int32_t i = base + tid;
       const bool valid = i < V_high;
-      uint64_t e = 0;
-      uint32_t dg = 0;
-      if (valid) {
-        e = src[i];
-        dg = (((~(uint32_t)(e >> 32)) & kmask) >> sh) & 255u;
-      }
+      const uint64_t e = e_next;
+      e_next = i + kSelThreads < V_high ? src[i + kSelThreads] : 0ull;
+      const uint32_t dg = valid ? (((~(uint32_t)(e >> 32)) & kmask) >> sh) & 255u : 0u;
       uint64_t peers = __ballot(valid);
 #pragma unroll
       for (int b = 0; b < 8; ++b) {
@@ -233,12 +317,22 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   __threadfence_block();
   __syncthreads();
   unsigned long long sel = 0;
-  for (int32_t i = tid; i < V_high; i += kSelThreads) {
-    const uint64_t e = src[i];
-    const int32_t id = (int32_t)(uint32_t)e;
-    t2f[i] = id;
-    if (f2t && (uint32_t)id < (uint32_t)V) f2t[id] = i;
-    sel += e >> 32;
+  for (int32_t base = 0; base < V_high; base += kUnroll * kSelThreads) {
+    uint64_t e[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int32_t i = base + u * kSelThreads + tid;
+      e[u] = i < V_high ? src[i] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int32_t i = base + u * kSelThreads + tid;
+      if (i >= V_high) continue;
+      const int32_t id = (int32_t)(uint32_t)e[u];
+      t2f[i] = id;
+      if (f2t && (uint32_t)id < (uint32_t)V) f2t[id] = i;
+      sel += e[u] >> 32;
+    }
   }
   sel = block_sum_u64(sel, s);
   if (tid == 0) {

@@ -99,7 +99,7 @@ int vt_count_freq(const int32_t *ids, uint64_t n, int32_t V, uint32_t *counts,
  * Coverage is sel_sum / tot_sum (the caller divides; tot_sum == 0 means no
  * id was counted).
  *
- * counts  device, uint32[V]
+ * counts  device, uint32[V], 16-byte aligned
  * V, V_high  1 <= V_high <= V < 2^31
  * t2f     device, int32[V_high]
  * f2t     device, int32[V], or NULL to skip it

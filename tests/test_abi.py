@@ -84,6 +84,7 @@ def test_select_validation(lib):
     assert f(A, 100, 101, A, A, A, A, A, 10**9, None) == INVALID         # V_high > V
     assert f(A, 100, 0, A, A, A, A, A, 10**9, None) == INVALID
     assert f(None, 100, 10, A, A, A, A, A, 10**9, None) == INVALID
+    assert f(A + 4, 100, 10, A, A, A, A, A, 10**9, None) == INVALID     # misaligned counts
     assert f(A, 100, 10, None, A, A, A, A, 10**9, None) == INVALID
     assert f(A, 100, 10, A, A, None, A, A, 10**9, None) == INVALID
     assert f(A, 4096, 1024, A, None, A, A, A, n - 1, None) == WORKSPACE
