@@ -81,12 +81,17 @@ __device__ __forceinline__ uint32_t block_rank(const uint64_t *keys,
     const int r = wave % NR, part = wave / NR;
     const uint64_t v = keys[r * kWave + lane];
     const uint64_t *kr = keys + r * kWave + part * SPAN;
+    // Broadcast reads in batches of up to 16, all issued before the compares.
+    constexpr int B = SPAN / 2 < 16 ? SPAN / 2 : 16;
     uint32_t c = 0;
 #pragma unroll
-    for (int j = 0; j < SPAN; j += 2) {
-      const u64x2 q = *reinterpret_cast<const u64x2 *>(kr + j);
-      c += q.x > v;
-      c += q.y > v;
+    for (int j0 = 0; j0 < SPAN / 2; j0 += B) {
+      u64x2 q[B];
+#pragma unroll
+      for (int j = 0; j < B; ++j) q[j] = *reinterpret_cast<const u64x2 *>(kr + 2 * (j0 + j));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < B; ++j) c += (q[j].x > v) + (q[j].y > v);
     }
     prank[(part * NR + r) * kWave + lane] = c;
   }
@@ -422,12 +427,17 @@ __device__ __forceinline__ void wave_publish_tile(const HeadArgs &a, int m, int 
   sc[lane] = key;
   top[lane] = 0;
   __builtin_amdgcn_wave_barrier();
+  // Rank by counting larger keys: 32 broadcast reads, issued in two batches
+  // of 16 so that their LDS latencies overlap.
   uint32_t rank = 0;
 #pragma unroll
-  for (int j = 0; j < kWave; j += 2) {
-    const u64x2 q = *reinterpret_cast<const u64x2 *>(sc + j);
-    rank += q.x > key;
-    rank += q.y > key;
+  for (int half = 0; half < 2; ++half) {
+    u64x2 q[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) q[j] = *reinterpret_cast<const u64x2 *>(sc + half * 32 + 2 * j);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) rank += (q[j].x > key) + (q[j].y > key);
   }
   if (rank < (uint32_t)k) top[rank] = key;
   __builtin_amdgcn_wave_barrier();
@@ -454,6 +464,7 @@ __device__ __forceinline__ void wave_publish_tile(const HeadArgs &a, int m, int 
 constexpr int kStageChunks = 16;                      // 16-byte chunks per row and stage
 constexpr int kStagePitch = kStageChunks + 1;         // row pitch in chunks
 constexpr int kStageSize = kTileRows * kStagePitch;   // chunks per wave
+constexpr int kPartPitch = kTileRows + 4;             // floats per partial-sum row
 
 // h re-laid out in B-operand order, so that each B load of the MFMA loop
 // reads 1 KiB contiguous: hp[(s * NT + cb) * 64 + l] = the 16-byte chunk
@@ -470,7 +481,7 @@ template <int NT>
 __global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a) {
   union alignas(16) Smem {
     u32x4 stage[kMfmaWaves][kStageSize];
-    float part[kMfmaWaves][NT * 16][kTileRows];
+    float part[kMfmaWaves][NT * 16][kPartPitch];
   };
   __shared__ Smem sm;
   __shared__ alignas(16) uint64_t s_sc[kMfmaWaves][2][kWave];
@@ -538,21 +549,22 @@ __global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a
   }
   __syncthreads();  // every wave is done with its stage before part[] reuses it
 
-  // Partial products to LDS as [draft row][tile row], then a fixed-order sum
-  // over the waves into wave 0's slot.
+  // Partial products to LDS as [draft row][tile row] (rows padded to break
+  // bank conflicts; each accumulator is 4 consecutive tile rows), then a
+  // fixed-order sum over the waves into wave 0's slot.
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
     for (int cb = 0; cb < NT; ++cb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sm.part[wave][cb * 16 + r16][rb * 16 + 4 * g + r] = acc[rb][cb][r];
+      *reinterpret_cast<f32x4 *>(&sm.part[wave][cb * 16 + r16][rb * 16 + 4 * g]) = acc[rb][cb];
   __syncthreads();
-  float *z0 = &sm.part[0][0][0];
-  for (int i = threadIdx.x; i < NT * 16 * kTileRows; i += kMfmaWaves * kWave) {
-    float val = z0[i];
+  for (int i = threadIdx.x; i < NT * 16 * (kTileRows / 4); i += kMfmaWaves * kWave) {
+    const int row = i / (kTileRows / 4), c4 = 4 * (i % (kTileRows / 4));
+    f32x4 val = *reinterpret_cast<const f32x4 *>(&sm.part[0][row][c4]);
 #pragma unroll
-    for (int w = 1; w < kMfmaWaves; ++w) val += (&sm.part[w][0][0])[i];
-    z0[i] = val;
+    for (int w = 1; w < kMfmaWaves; ++w)
+      val += *reinterpret_cast<const f32x4 *>(&sm.part[w][row][c4]);
+    *reinterpret_cast<f32x4 *>(&sm.part[0][row][c4]) = val;
   }
   __syncthreads();
 
