@@ -52,9 +52,14 @@ def _load():
             lib.or_softmax.argtypes = [P, i32, i32, P, P, P]
             lib.or_topk.argtypes = [P, P, i32, i32, i32, P, P]
             lib.or_draft_head.argtypes = [P, i32, i32, P, i32, P, i32, P, P, P, P, P]
+            lib.or_draft_sample.argtypes = [P, i32, i32, P, i32, P, u64, u64, P, P, P, P]
+            lib.or_philox4x32_10.argtypes = [P, P, P]
+            lib.or_philox4x32_10.restype = None
+            lib.or_gumbel.argtypes = [u64, u64, i32, i32]
+            lib.or_gumbel.restype = C.c_double
             lib.or_threads.argtypes = []
             for f in (lib.or_threads, lib.or_count, lib.or_select, lib.or_gather, lib.or_logits,
-                      lib.or_softmax, lib.or_topk, lib.or_draft_head):
+                      lib.or_softmax, lib.or_topk, lib.or_draft_head, lib.or_draft_sample):
                 f.restype = C.c_int
             _lib = lib
     return _lib
@@ -186,3 +191,48 @@ def draft_head(h, W_trim, t2f, k: int, want_logits: bool = False):
     if want_logits:
         return ids, probs, (z, mu, S)
     return ids, probs
+
+
+def philox4x32_10(ctr, key):
+    """Philox4x32-10 (Salmon et al., SC 2011) of one counter and key."""
+    c = np.asarray(ctr, np.uint32).reshape(4).copy()
+    k = np.asarray(key, np.uint32).reshape(2).copy()
+    out = np.empty(4, np.uint32)
+    _load().or_philox4x32_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def gumbel(seed: int, offset: int, M: int, n: int):
+    """The Gumbel variates G[m, j] of a draw keyed by (seed, offset)."""
+    lib = _load()
+    g = np.empty((M, n), np.float64)
+    for m in range(M):
+        for j in range(n):
+            g[m, j] = lib.or_gumbel(C.c_uint64(seed), C.c_uint64(offset), m, j)
+    return g
+
+
+def draft_sample(h, W_trim, t2f, seed: int, offset: int, want_logits: bool = False):
+    """One multinomial draw per row from the subset softmax (Gumbel-max with
+    Philox uniforms), remapped through t2f (VocabTrim page, Step 4).
+
+    Returns ``(full_ids int32[M], probs float32[M], trimmed index int32[M])``
+    and, with ``want_logits``, also ``z fp64[M, V_high]``.
+    """
+    h = _arr(h, np.uint16, 2)
+    W_trim = _arr(W_trim, np.uint16, 2)
+    t2f = _arr(t2f, np.int32, 1)
+    M, d = h.shape
+    V_high = W_trim.shape[0]
+    if W_trim.shape[1] != d or t2f.size != V_high:
+        raise ValueError("shape mismatch")
+    ids = np.empty(M, np.int32)
+    probs = np.empty(M, np.float32)
+    ti = np.empty(M, np.int32)
+    z = np.empty((M, V_high), np.float64) if want_logits else None
+    _ok(_load().or_draft_sample(_p(h), M, d, _p(W_trim), V_high, _p(t2f), C.c_uint64(seed),
+                                C.c_uint64(offset), _p(ids), _p(probs), _p(ti), _p(z)),
+        "draft_sample")
+    if want_logits:
+        return ids, probs, ti, z
+    return ids, probs, ti

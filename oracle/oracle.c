@@ -13,6 +13,8 @@
  *   [FR]  "FR-Spec: Accelerating Large-Vocabulary Language Models via
  *         Frequency-Ranked Speculative Sampling" paper notes:
  *         Method / key design "frequency-ranked vocabulary compression".
+ *   [VT] Step 4's draft loop samples one token from the subset softmax
+ *         (a multinomial draw) and maps it back to its full id.
  *
  * Precision: every floating-point step is done in double (fp64); bfloat16
  * inputs are widened exactly. Results do not depend on the OpenMP thread
@@ -23,9 +25,13 @@
  *   - ids outside [0, V) are not counted; they are tallied in n_invalid.
  *   - ranking is by count descending, ties by lower id; every id in [0, V)
  *     is eligible, including ids never seen (count 0).
- *   - the draft row's pick is a deterministic top-k (ties: lower full id),
- *     not the page's multinomial draw; probabilities are the softmax over
- *     the kept subset, not renormalised over the top k; temperature 1.
+ *   - the draft row's pick is a deterministic top-k (ties: lower full id);
+ *     probabilities are the softmax over the kept subset, not renormalised
+ *     over the top k; temperature 1.
+ *   - the page's multinomial draw (or_draft_sample) is a Gumbel-max draw
+ *     whose uniforms come from the counter-based generator Philox4x32-10
+ *     (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as
+ *     1, 2, 3", SC 2011), one generator call per (row, trimmed index).
  *
  * Parity pins: every function here is pinned by the CPU tests against
  * library routines, closed forms, brute force or hand-worked examples.
@@ -299,5 +305,102 @@ done:
     free(mu);
     free(S);
     free(ti);
+    return rc;
+}
+
+/* Philox4x32-10 (Salmon et al., SC 2011): a 4 x 32-bit counter and a
+ * 2 x 32-bit key; each of the 10 rounds multiplies words 0 and 2 by two
+ * fixed odd constants (full 64-bit products), swaps the halves and mixes in
+ * the other words and the key; the key is advanced by two Weyl constants
+ * between rounds. */
+void or_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2],
+                      uint32_t out[4])
+{
+    uint32_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+    uint32_t k0 = key_in[0], k1 = key_in[1];
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+        const uint32_t n0 = hi1 ^ c1 ^ k0, n1 = lo1, n2 = hi0 ^ c3 ^ k1, n3 = lo0;
+        c0 = n0;
+        c1 = n1;
+        c2 = n2;
+        c3 = n3;
+    }
+    out[0] = c0;
+    out[1] = c1;
+    out[2] = c2;
+    out[3] = c3;
+}
+
+/* The Gumbel variate of draft row m and trimmed index j for a draw keyed by
+ * (seed, offset): Philox4x32-10 with counter (j, m, offset low, offset high)
+ * and key (seed low, seed high); the top 24 bits x of its first word give
+ * the uniform u = (x + 1/2) / 2^24 in (0, 1), exactly representable; the
+ * variate is -log(-log u). */
+double or_gumbel(uint64_t seed, uint64_t offset, int32_t m, int32_t j)
+{
+    const uint32_t ctr[4] = {(uint32_t)j, (uint32_t)m, (uint32_t)offset,
+                             (uint32_t)(offset >> 32)};
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t o[4];
+    or_philox4x32_10(ctr, key, o);
+    const double u = ((double)(o[0] >> 8) + 0.5) / 16777216.0;
+    return -log(-log(u));
+}
+
+/* One sampled draft token per row, the page's multinomial draw from the
+ * subset softmax ([VT] Step 4's draft loop), by the Gumbel-max rule: the
+ * draw is argmax_j (z[m, j] + G[m, j]) with independent standard Gumbel
+ * variates G, which picks j with probability exp(z_j) / sum_i exp(z_i).
+ * Equal perturbed logits: the lower full id. Outputs:
+ *   full_ids[m] = t2f[j*],  probs[m] = p[m, j*] (subset softmax, float)
+ *   trim_idx[m] = j* (may be NULL); z_out [M, V_high] (may be NULL). */
+int or_draft_sample(const uint16_t *h, int32_t M, int32_t d,
+                    const uint16_t *W_trim, int32_t V_high, const int32_t *t2f,
+                    uint64_t seed, uint64_t offset, int32_t *full_ids,
+                    float *probs, int32_t *trim_idx, double *z_out)
+{
+    if (!h || !W_trim || !t2f || !full_ids || !probs || M <= 0 || d <= 0 ||
+        V_high <= 0)
+        return OR_BAD;
+    double *z = z_out ? z_out
+                      : (double *)malloc(sizeof(double) * (size_t)M * V_high);
+    double *mu = (double *)malloc(sizeof(double) * (size_t)M);
+    double *S = (double *)malloc(sizeof(double) * (size_t)M);
+    int rc = OR_BAD;
+    if (!z || !mu || !S)
+        goto done;
+    if ((rc = or_logits(h, M, d, W_trim, V_high, z)) != OR_OK)
+        goto done;
+    if ((rc = or_softmax(z, M, V_high, NULL, mu, S)) != OR_OK)
+        goto done;
+    for (int32_t m = 0; m < M; ++m) {
+        const double *zm = z + (size_t)m * V_high;
+        int32_t best = 0;
+        double bv = zm[0] + or_gumbel(seed, offset, m, 0);
+        for (int32_t j = 1; j < V_high; ++j) {
+            const double v = zm[j] + or_gumbel(seed, offset, m, j);
+            if (v > bv || (v == bv && t2f[j] < t2f[best])) {
+                bv = v;
+                best = j;
+            }
+        }
+        full_ids[m] = t2f[best];
+        probs[m] = (float)(exp(zm[best] - mu[m]) / S[m]);
+        if (trim_idx)
+            trim_idx[m] = best;
+    }
+done:
+    if (!z_out)
+        free(z);
+    free(mu);
+    free(S);
     return rc;
 }
