@@ -26,7 +26,7 @@ import torch
 __all__ = [
     "VtError", "lib", "lib_path", "VT_K_MAX", "VT_M_MAX", "VT_D_MAX",
     "VT_VHIGH_MAX", "vt_count_freq", "vt_select_vocab", "vt_gather_head",
-    "vt_draft_head", "vt_head_logits", "vt_count_freq_workspace_size",
+    "vt_draft_head", "vt_draft_sample", "vt_head_logits", "vt_count_freq_workspace_size",
     "vt_select_vocab_workspace_size", "vt_draft_head_workspace_size",
     "coverage",
 ]
@@ -51,6 +51,7 @@ _SIGS = {
     "vt_gather_head": (_INT, [_P, _I32, _I32, _P, _I32, _P, _P, _P]),
     "vt_draft_head_workspace_size": (_SZ, [_I32, _I32, _I32, _I32]),
     "vt_draft_head": (_INT, [_P, _I32, _I32, _P, _I32, _P, _I32, _P, _P, _P, _SZ, _P]),
+    "vt_draft_sample": (_INT, [_P, _I32, _I32, _P, _I32, _P, _U64, _U64, _P, _P, _P, _SZ, _P]),
     "vt_head_logits": (_INT, [_P, _I32, _I32, _P, _I32, _P, _P]),
 }
 
@@ -230,6 +231,37 @@ def vt_draft_head(h: torch.Tensor, W_trim: torch.Tensor, t2f: torch.Tensor, k: i
     _check(lib().vt_draft_head(_ptr(h), M, d, _ptr(W_trim), V_high, _ptr(t2f), k,
                                _ptr(full_ids), _ptr(probs), _ptr(ws), ws.numel(), _stream(h)),
            "vt_draft_head")
+    return full_ids, probs
+
+
+def vt_draft_sample(h: torch.Tensor, W_trim: torch.Tensor, t2f: torch.Tensor, seed: int,
+                    offset: int, full_ids: torch.Tensor | None = None,
+                    probs: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """One sampled draft token per row (VocabTrim Step 4's multinomial draw,
+    remapped): (full_ids[M], probs[M])."""
+    _dev(h, "h", _BF16, 2)
+    _dev(W_trim, "W_trim", _BF16, 2)
+    _dev(t2f, "t2f", (torch.int32,), 1)
+    M, d = h.shape
+    V_high = W_trim.shape[0]
+    if W_trim.shape[1] != d or t2f.numel() != V_high:
+        raise ValueError("shape mismatch between h, W_trim and t2f")
+    dev = h.device
+    if full_ids is None:
+        full_ids = torch.empty(M, dtype=torch.int32, device=dev)
+    if probs is None:
+        probs = torch.empty(M, dtype=torch.float32, device=dev)
+    _dev(full_ids, "full_ids", (torch.int32,))
+    _dev(probs, "probs", (torch.float32,))
+    if full_ids.numel() != M or probs.numel() != M:
+        raise ValueError("outputs must hold M entries")
+    if ws is None:
+        need = vt_draft_head_workspace_size(M, V_high, d, 1)
+        ws = _workspace(dev, "head", need, True)
+    _check(lib().vt_draft_sample(_ptr(h), M, d, _ptr(W_trim), V_high, _ptr(t2f),
+                                 int(seed) & (2 ** 64 - 1), int(offset) & (2 ** 64 - 1),
+                                 _ptr(full_ids), _ptr(probs), _ptr(ws), ws.numel(), _stream(h)),
+           "vt_draft_sample")
     return full_ids, probs
 
 

@@ -132,6 +132,21 @@ int vt_draft_head(const uint16_t *h, int32_t M, int32_t d,
                                           as_stream(stream)));
 }
 
+int vt_draft_sample(const uint16_t *h, int32_t M, int32_t d,
+                    const uint16_t *W_trim, int32_t V_high, const int32_t *t2f,
+                    uint64_t seed, uint64_t offset, int32_t *full_ids,
+                    float *probs, void *ws, size_t ws_bytes, void *stream) {
+  int st = check_head(h, M, d, W_trim, V_high);
+  if (st != VT_OK) return st;
+  if (!t2f || !full_ids) return VT_ERR_INVALID_ARG;
+  if (!ws || !aligned(ws, 256) ||
+      ws_bytes < vt_draft_head_workspace_size(M, V_high, d, 1))
+    return VT_ERR_WORKSPACE;
+  return hip_status(vt::launch_draft_sample(h, M, d, W_trim, V_high, t2f, seed,
+                                            offset, full_ids, probs, ws,
+                                            as_stream(stream)));
+}
+
 int vt_head_logits(const uint16_t *h, int32_t M, int32_t d,
                    const uint16_t *W_trim, int32_t V_high, float *logits,
                    void *stream) {

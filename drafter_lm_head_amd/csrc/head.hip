@@ -41,6 +41,10 @@ struct HeadArgs {
   float *probs;          // [M][k]
   float *logits;         // [M][V_high], logits-only variant
   const u32x4 *hp;       // h in MFMA B-operand order (MFMA path)
+  // Sampling mode (k = 1): the pick is the largest z + Gumbel(seed, offset).
+  int32_t sample;
+  uint32_t seed_lo, seed_hi, off_lo, off_hi;
+  uint64_t *tile_z;      // [M][tiles]: bits of z of each tile's drawn row
 };
 
 __device__ __forceinline__ uint64_t pack_ms(float mu, float S) {
@@ -48,6 +52,34 @@ __device__ __forceinline__ uint64_t pack_ms(float mu, float S) {
 }
 __device__ __forceinline__ float ms_max(uint64_t v) { return __uint_as_float((uint32_t)v); }
 __device__ __forceinline__ float ms_sum(uint64_t v) { return __uint_as_float((uint32_t)(v >> 32)); }
+
+// The sampling key of tile row j of draft row m: (z + G) in key order, then
+// the lower full id; the draw is the largest key over all rows.
+__device__ __forceinline__ uint64_t sample_key(const HeadArgs &a, int m, int j, float z,
+                                               int32_t fid) {
+  return make_key(z + gumbel(a.seed_lo, a.seed_hi, a.off_lo, a.off_hi, m, j), fid);
+}
+
+// Sampling-mode tile partial of one draft row, by one wave (lane = tile row):
+// the tile's largest sampling key and that row's z, and the tile's softmax
+// partial over the unperturbed z.
+__device__ __forceinline__ void wave_publish_sample(const HeadArgs &a, int m, int tile,
+                                                    int row0, float z, int32_t fid,
+                                                    bool valid) {
+  const int lane = __lane_id();
+  const uint64_t key = valid ? sample_key(a, m, row0 + lane, z, fid) : 0ull;
+  const uint64_t best = wave_max_u64(key);
+  const uint64_t hit = __ballot(valid && key == best);
+  const float zb = __shfl(z, hit ? (int)__builtin_ctzll(hit) : 0);
+  const float mu = wave_max(valid ? z : -INFINITY);
+  const float S = wave_sum(valid ? __expf(z - mu) : 0.f);
+  if (lane == 0) {
+    publish_u64(a.tile_keys + (size_t)m * a.tiles + tile, best);
+    publish_u64(a.tile_z + (size_t)m * a.tiles + tile, __float_as_uint(zb));
+    publish_u64(a.tile_ms + (size_t)m * a.tiles + tile, pack_ms(mu, S));
+  }
+}
+
 
 constexpr int kMaxTiles = VT_VHIGH_MAX / kTileRows;
 
@@ -60,7 +92,7 @@ struct alignas(16) MergeShared {
   uint32_t prank[4][4][kWave];               // partial ranks
   unsigned long long kmax, T;
   uint32_t cnt;
-  float f[WAVES];
+  float f[WAVES], f2[WAVES], zw[WAVES];
 };
 
 // Ranks (0 = largest) of NR rows of 64 keys in LDS, keys[r * 64 + lane],
@@ -81,17 +113,12 @@ __device__ __forceinline__ uint32_t block_rank(const uint64_t *keys,
     const int r = wave % NR, part = wave / NR;
     const uint64_t v = keys[r * kWave + lane];
     const uint64_t *kr = keys + r * kWave + part * SPAN;
-    // Broadcast reads in batches of up to 16, all issued before the compares.
-    constexpr int B = SPAN / 2 < 16 ? SPAN / 2 : 16;
     uint32_t c = 0;
 #pragma unroll
-    for (int j0 = 0; j0 < SPAN / 2; j0 += B) {
-      u64x2 q[B];
-#pragma unroll
-      for (int j = 0; j < B; ++j) q[j] = *reinterpret_cast<const u64x2 *>(kr + 2 * (j0 + j));
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < B; ++j) c += (q[j].x > v) + (q[j].y > v);
+    for (int j = 0; j < SPAN; j += 2) {
+      const u64x2 q = *reinterpret_cast<const u64x2 *>(kr + j);
+      c += q.x > v;
+      c += q.y > v;
     }
     prank[(part * NR + r) * kWave + lane] = c;
   }
@@ -147,6 +174,83 @@ __device__ void block_sort_desc(uint64_t *cand, uint32_t n) {
 //     dozen, are collected in LDS and ranked. With more than 64 survivors
 //     (exact ties, large k) a workgroup sort or, past kCandCap, k exact
 //     max rounds take over.
+// Sampling-mode merge of draft row m: the largest published key (the draw)
+// with its row's z, and the softmax max and sum over the tile partials in a
+// fixed order; full_ids[m] and probs[m] = exp(z - max) / sum.
+template <int WAVES>
+__device__ void sample_merge(const HeadArgs &a, int m, MergeShared<WAVES> &sh) {
+  constexpr int NT = WAVES * kWave;
+  const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
+  const int tiles = a.tiles;
+  const uint64_t *keys = a.tile_keys + (size_t)m * tiles;
+  const uint64_t *zs = a.tile_z + (size_t)m * tiles;
+  const uint64_t *ms = a.tile_ms + (size_t)m * tiles;
+  uint64_t best = 0;
+  float zb = 0.f, mu_l = -INFINITY;
+  // The thread's tiles in index order: keys, their z, softmax partials.
+  constexpr int kB = 4;
+  uint64_t ms_keep[kB];
+  for (int base = 0; base < tiles; base += kB * NT) {
+    uint64_t kv[kB], zv[kB];
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      const int t = base + tid + j * NT;
+      kv[j] = t < tiles ? fetch_u64(keys + t) : 0ull;
+      zv[j] = t < tiles ? fetch_u64(zs + t) : 0ull;
+      ms_keep[j] = t < tiles ? fetch_u64(ms + t) : 0ull;
+    }
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      if (kv[j] > best) {
+        best = kv[j];
+        zb = __uint_as_float((uint32_t)zv[j]);
+      }
+      if (base + tid + j * NT < tiles) mu_l = fmaxf(mu_l, ms_max(ms_keep[j]));
+    }
+  }
+  const float mu_w = wave_max(mu_l);
+  float s_l = 0.f;
+  for (int base = 0; base < tiles; base += kB * NT) {
+    if (tiles > kB * NT)  // more than one round: reload (else still in registers)
+#pragma unroll
+      for (int j = 0; j < kB; ++j) {
+        const int t = base + tid + j * NT;
+        ms_keep[j] = t < tiles ? fetch_u64(ms + t) : 0ull;
+      }
+#pragma unroll
+    for (int j = 0; j < kB; ++j)
+      if (base + tid + j * NT < tiles) s_l += ms_sum(ms_keep[j]) * __expf(ms_max(ms_keep[j]) - mu_w);
+  }
+  const float s_w = wave_sum(s_l);
+  const uint64_t bw = wave_max_u64(best);
+  const uint64_t hit = __ballot(best == bw && bw != 0ull);
+  const float zw = __shfl(zb, hit ? (int)__builtin_ctzll(hit) : 0);
+  if (lane == 0) {
+    sh.sc[0][wave] = bw;
+    sh.f[wave] = mu_w;
+    sh.f2[wave] = s_w;
+    sh.zw[wave] = zw;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float mu = sh.f[0];
+    for (int w = 1; w < WAVES; ++w) mu = fmaxf(mu, sh.f[w]);
+    float S = 0.f;
+    uint64_t kbest = 0;
+    float z = 0.f;
+    for (int w = 0; w < WAVES; ++w) {
+      if (sh.f[w] != -INFINITY) S += sh.f2[w] * __expf(sh.f[w] - mu);
+      if (sh.sc[0][w] > kbest) {
+        kbest = sh.sc[0][w];
+        z = sh.zw[w];
+      }
+    }
+    a.full_ids[m] = key_id(kbest);
+    if (a.probs) a.probs[m] = __expf(z - mu) / S;
+  }
+  __syncthreads();  // sh is reused by the next draft row's merge
+}
+
 template <int WAVES>
 __device__ void final_merge(const HeadArgs &a, int m, MergeShared<WAVES> &sh) {
   constexpr int NT = WAVES * kWave;
@@ -365,9 +469,17 @@ __global__ __launch_bounds__(WAVES *kWave) void head_gemv_kernel(HeadArgs a) {
   if (LOGITS) return;
   __syncthreads();
 
+  const bool valid = row0 + lane < a.V_high;
+  if (a.sample) {  // one draw per draft row
+    if (wave < MT) wave_publish_sample(a, wave, tile, row0, s_z[wave][lane], fid, valid);
+    if (arrive(a.counter, &s_slot) != (uint32_t)(a.tiles - 1)) return;
+    for (int m = 0; m < MT; ++m) sample_merge<WAVES>(a, m, sh);
+    if (threadIdx.x == 0) reset_counter(a.counter);
+    return;
+  }
+
   // Tile partial: top-k keys and softmax partial of each draft row.
   const int k = a.k;
-  const bool valid = row0 + lane < a.V_high;
   uint64_t *s_key = sh.cand;               // [MT][64] keys of the tile
   uint64_t *s_top = sh.cand + MT * kWave;  // [MT][64] ranked keys
   if (wave < MT) {
@@ -572,6 +684,10 @@ __global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a
   const int32_t fid = valid ? a.t2f[row0 + lane] : 0;
   for (int m = wave; m < M; m += kMfmaWaves) {
     const float z = sm.part[0][m][lane];
+    if (a.sample) {
+      wave_publish_sample(a, m, tile, row0, z, fid, valid);
+      continue;
+    }
     wave_publish_tile(a, m, tile, valid ? make_key(z, fid) : 0ull, z, valid,
                       s_sc[wave][0], s_sc[wave][1]);
   }
@@ -581,7 +697,10 @@ __global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a
 template <int WAVES>
 __global__ __launch_bounds__(WAVES *kWave) void head_merge_kernel(HeadArgs a) {
   __shared__ MergeShared<WAVES> sh;
-  final_merge<WAVES>(a, blockIdx.x, sh);
+  if (a.sample)
+    sample_merge<WAVES>(a, blockIdx.x, sh);
+  else
+    final_merge<WAVES>(a, blockIdx.x, sh);
 }
 
 template <int NT>
@@ -650,16 +769,19 @@ HeadPlan head_plan(int32_t M, int32_t V_high, int32_t k) {
   off += align_up((size_t)M * p.tiles * k * 8, 256);
   p.off_tile_ms = off;
   off += align_up((size_t)M * p.tiles * 8, 256);
+  p.off_tile_z = off;  // sampling mode: z of each tile's drawn row
+  off += align_up((size_t)M * p.tiles * 8, 256);
   p.off_hpack = off;  // MFMA path: h in B-operand order, 16 * NT rows x d
   off += M > kGemvMaxRows ? align_up((size_t)((M + 15) / 16) * 16 * (size_t)VT_D_MAX * 2, 256) : 0;
   p.bytes = off;
   return p;
 }
 
-hipError_t launch_draft_head(const uint16_t *h, int32_t M, int32_t d,
-                             const uint16_t *W_trim, int32_t V_high,
-                             const int32_t *t2f, int32_t k, int32_t *full_ids,
-                             float *probs, void *ws, hipStream_t stream) {
+namespace {
+hipError_t launch_head_call(const uint16_t *h, int32_t M, int32_t d, const uint16_t *W_trim,
+                            int32_t V_high, const int32_t *t2f, int32_t k, int32_t *full_ids,
+                            float *probs, void *ws, bool sample, uint64_t seed,
+                            uint64_t offset, hipStream_t stream) {
   const HeadPlan p = head_plan(M, V_high, k);
   char *base = static_cast<char *>(ws);
   HeadArgs a{};
@@ -680,6 +802,12 @@ hipError_t launch_draft_head(const uint16_t *h, int32_t M, int32_t d,
   a.h = reinterpret_cast<const u32x4 *>(h);
   a.full_ids = full_ids;
   a.probs = probs;
+  a.sample = sample ? 1 : 0;
+  a.seed_lo = (uint32_t)seed;
+  a.seed_hi = (uint32_t)(seed >> 32);
+  a.off_lo = (uint32_t)offset;
+  a.off_hi = (uint32_t)(offset >> 32);
+  a.tile_z = reinterpret_cast<uint64_t *>(base + p.off_tile_z);
   // Up to kGemvMaxRows rows: one GEMV pass with the merge in the same
   // kernel. More rows: the MFMA skinny GEMM, then one merge workgroup per row.
   if (M <= kGemvMaxRows) return launch_gemv(a, stream);
@@ -689,6 +817,23 @@ hipError_t launch_draft_head(const uint16_t *h, int32_t M, int32_t d,
     case 3: return launch_mfma<3>(a, stream);
     default: return launch_mfma<4>(a, stream);
   }
+}
+}  // namespace
+
+hipError_t launch_draft_head(const uint16_t *h, int32_t M, int32_t d,
+                             const uint16_t *W_trim, int32_t V_high,
+                             const int32_t *t2f, int32_t k, int32_t *full_ids,
+                             float *probs, void *ws, hipStream_t stream) {
+  return launch_head_call(h, M, d, W_trim, V_high, t2f, k, full_ids, probs, ws, false, 0, 0,
+                          stream);
+}
+
+hipError_t launch_draft_sample(const uint16_t *h, int32_t M, int32_t d,
+                               const uint16_t *W_trim, int32_t V_high, const int32_t *t2f,
+                               uint64_t seed, uint64_t offset, int32_t *full_ids,
+                               float *probs, void *ws, hipStream_t stream) {
+  return launch_head_call(h, M, d, W_trim, V_high, t2f, 1, full_ids, probs, ws, true, seed,
+                          offset, stream);
 }
 
 hipError_t launch_head_logits(const uint16_t *h, int32_t M, int32_t d,

@@ -137,6 +137,40 @@ __device__ __forceinline__ int32_t key_id(uint64_t key) {
   return (int32_t)(~(uint32_t)key);
 }
 
+// ------------------------------------------------------------- sampling
+// Counter-based uniforms: Philox4x32-10 (Salmon, Moraes, Dror and Shaw,
+// "Parallel random numbers: as easy as 1, 2, 3", SC 2011). Ten rounds of two
+// 32 x 32 -> 64-bit products of words 0 and 2 with fixed odd multipliers,
+// half swaps and key mixing; the key advances by two Weyl increments between
+// rounds. Only the first output word is used here.
+__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                 uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c0;
+}
+
+// Standard Gumbel variate of draft row m and trimmed index j for the draw
+// keyed by (seed, offset): counter (j, m, offset), key seed; the top 24 bits
+// x of the first word give u = (x + 1/2) / 2^24 in (0, 1) (exact in fp32),
+// and the variate is -log(-log u).
+__device__ __forceinline__ float gumbel(uint32_t seed_lo, uint32_t seed_hi, uint32_t off_lo,
+                                        uint32_t off_hi, int m, int j) {
+  const uint32_t x = philox_word0((uint32_t)j, (uint32_t)m, off_lo, off_hi, seed_lo, seed_hi);
+  const float u = ((float)(x >> 8) + 0.5f) * 0x1p-24f;
+  return -logf(-logf(u));
+}
+
 // Sorts one key per lane so that lane 0 holds the largest (bitonic network).
 __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key) {
   const int lane = __lane_id();

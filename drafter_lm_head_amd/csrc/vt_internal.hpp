@@ -40,7 +40,7 @@ hipError_t launch_gather(const uint16_t *W, int32_t V, int32_t d,
 constexpr int kTileRows = 64;
 struct HeadPlan {
   int32_t tiles;
-  size_t off_group, zero_bytes, off_tile_keys, off_tile_ms, off_hpack;
+  size_t off_group, zero_bytes, off_tile_keys, off_tile_ms, off_tile_z, off_hpack;
   size_t bytes;
 };
 HeadPlan head_plan(int32_t M, int32_t V_high, int32_t k);
@@ -48,6 +48,10 @@ hipError_t launch_draft_head(const uint16_t *h, int32_t M, int32_t d,
                              const uint16_t *W_trim, int32_t V_high,
                              const int32_t *t2f, int32_t k, int32_t *full_ids,
                              float *probs, void *ws, hipStream_t stream);
+hipError_t launch_draft_sample(const uint16_t *h, int32_t M, int32_t d,
+                               const uint16_t *W_trim, int32_t V_high, const int32_t *t2f,
+                               uint64_t seed, uint64_t offset, int32_t *full_ids,
+                               float *probs, void *ws, hipStream_t stream);
 hipError_t launch_head_logits(const uint16_t *h, int32_t M, int32_t d,
                               const uint16_t *W_trim, int32_t V_high,
                               float *logits, hipStream_t stream);

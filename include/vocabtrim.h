@@ -162,6 +162,31 @@ int vt_draft_head(const uint16_t *h, int32_t M, int32_t d,
                   int32_t k, int32_t *full_ids, float *probs, void *ws,
                   size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------------------ draft sample
+ * One draft token per row drawn from the subset softmax: the multinomial
+ * draw of [VT] Step 4's draft loop (softmax over the trimmed logits, one
+ * sample, then the trimmed index mapped back through trimmed_to_full).
+ * The draw is taken by the Gumbel-max rule, which selects index j with
+ * probability exp(z_j) / sum_i exp(z_i):
+ *   j*[m]       = argmax_j ( z[m, j] + G[m, j] )   (equal values: lower full id)
+ *   G[m, j]     = -log(-log u),  u = (x + 1/2) / 2^24, x = the top 24 bits of
+ *                 word 0 of Philox4x32-10 (Salmon et al., SC 2011) with
+ *                 counter (j, m, offset low, offset high), key (seed low, high)
+ *   full_ids[m] = t2f[j*[m]],   probs[m] = exp(z[m, j*] - mu) / S  (as above)
+ * z, mu and S are as for vt_draft_head (fp32 sums); G is computed in fp32.
+ * The draw is a function of (seed, offset, m, logits) only: repeated calls
+ * give identical results, and a caller advances `offset` once per draft
+ * step to get independent draws.
+ *
+ * h, d, W_trim, V_high, t2f, ws, ws_bytes, stream: as for vt_draft_head,
+ *           with ws of at least vt_draft_head_workspace_size(M, V_high, d, 1)
+ *           bytes (zero-filled once; every call leaves its counters at zero).
+ * full_ids  device, int32[M];  probs  device, float[M], or NULL to skip it */
+int vt_draft_sample(const uint16_t *h, int32_t M, int32_t d,
+                    const uint16_t *W_trim, int32_t V_high, const int32_t *t2f,
+                    uint64_t seed, uint64_t offset, int32_t *full_ids,
+                    float *probs, void *ws, size_t ws_bytes, void *stream);
+
 /* ------------------------------------------------------- logits (checks)
  * The trimmed logits alone, z[m, j] as defined for vt_draft_head, written to
  * logits (device, float[M, V_high]). For parity diagnostics: it writes the

@@ -57,6 +57,8 @@ def _load():
             lib.or_philox4x32_10.restype = None
             lib.or_gumbel.argtypes = [u64, u64, i32, i32]
             lib.or_gumbel.restype = C.c_double
+            lib.or_gumbel_block.argtypes = [u64, u64, i32, i32, P]
+            lib.or_gumbel_block.restype = C.c_int
             lib.or_threads.argtypes = []
             for f in (lib.or_threads, lib.or_count, lib.or_select, lib.or_gather, lib.or_logits,
                       lib.or_softmax, lib.or_topk, lib.or_draft_head, lib.or_draft_sample):
@@ -204,11 +206,8 @@ def philox4x32_10(ctr, key):
 
 def gumbel(seed: int, offset: int, M: int, n: int):
     """The Gumbel variates G[m, j] of a draw keyed by (seed, offset)."""
-    lib = _load()
     g = np.empty((M, n), np.float64)
-    for m in range(M):
-        for j in range(n):
-            g[m, j] = lib.or_gumbel(C.c_uint64(seed), C.c_uint64(offset), m, j)
+    _ok(_load().or_gumbel_block(C.c_uint64(seed), C.c_uint64(offset), M, n, _p(g)), "gumbel")
     return g
 
 

@@ -355,6 +355,18 @@ double or_gumbel(uint64_t seed, uint64_t offset, int32_t m, int32_t j)
     return -log(-log(u));
 }
 
+/* The variates G[m, j] of or_gumbel for all m < M, j < n, row-major. */
+int or_gumbel_block(uint64_t seed, uint64_t offset, int32_t M, int32_t n, double *g)
+{
+    if (!g || M <= 0 || n <= 0)
+        return OR_BAD;
+    for (int32_t m = 0; m < M; ++m)
+#pragma omp parallel for schedule(static)
+        for (int32_t j = 0; j < n; ++j)
+            g[(size_t)m * n + j] = or_gumbel(seed, offset, m, j);
+    return OR_OK;
+}
+
 /* One sampled draft token per row, the page's multinomial draw from the
  * subset softmax ([VT] Step 4's draft loop), by the Gumbel-max rule: the
  * draw is argmax_j (z[m, j] + G[m, j]) with independent standard Gumbel

@@ -99,3 +99,34 @@ def logit_bound(h, W):
     u = 2.0 ** -24
     gamma = d * u / (1 - d * u)
     return gamma * (hf @ Wf.T)
+
+
+def check_draws(ids_g, probs_g, h, W, t2f, seed, offset):
+    """Checks GPU draws (one per row) against the oracle's Gumbel-max draws
+    on the same (seed, offset). A different pick is accepted only where the
+    two candidates' perturbed logits z + G are within the fp32 error of the
+    GPU's z (Higham's bound) and of G and the sum (a few ulp of |z + G|);
+    probs are the oracle's subset-softmax value of the GPU's pick to 2e-3
+    absolute and 1e-4 relative. Returns the number of accepted near-ties."""
+    import oracle
+    ids_g = np.asarray(ids_g).ravel()
+    probs_g = np.asarray(probs_g, dtype=np.float64).ravel()
+    ids_o, probs_o, ti_o, z = oracle.draft_sample(h, W, t2f, seed, offset, want_logits=True)
+    M, n = z.shape
+    G = oracle.gumbel(seed, offset, M, n)
+    v = z + G
+    bound = logit_bound(h, W)
+    inv = inverse_map(t2f)
+    p = np.exp(z - z.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    near = 0
+    for m in range(M):
+        jg = inv[int(ids_g[m])]
+        jo = int(ti_o[m])
+        assert jg >= 0, f"row {m}: GPU drew a full id outside t2f"
+        if jg != jo:
+            tol = bound[m, jg] + bound[m, jo] + 4e-6 * (1.0 + abs(v[m, jo]))
+            assert v[m, jo] - v[m, jg] <= tol, (m, jo, jg, v[m, jo] - v[m, jg], tol)
+            near += 1
+        assert abs(probs_g[m] - p[m, jg]) <= 2e-3 + 1e-4 * p[m, jg], (m, probs_g[m], p[m, jg])
+    return near

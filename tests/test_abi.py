@@ -156,3 +156,25 @@ def test_binding_fails_loudly_without_gpu_tensors():
         dlh.vt_draft_head(torch.zeros((1, 8), dtype=torch.bfloat16),
                           torch.zeros((4, 8), dtype=torch.bfloat16),
                           torch.zeros(4, dtype=torch.int32), 2)
+
+
+def test_draft_sample_validation(lib):
+    n = lib.vt_draft_head_workspace_size(1, 32768, 4096, 1)
+    f = lib.vt_draft_sample
+    args = dict(h=A, M=1, d=4096, W=A, V_high=32768, t2f=A, seed=1, off=2, ids=A, probs=A,
+                ws=A, ws_n=n)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["h"], a["M"], a["d"], a["W"], a["V_high"], a["t2f"], a["seed"], a["off"],
+                 a["ids"], a["probs"], a["ws"], a["ws_n"], None)
+
+    assert call(M=0) == INVALID
+    assert call(M=65) == UNSUPPORTED
+    assert call(d=4100) == INVALID
+    assert call(V_high=0) == INVALID
+    assert call(h=A + 2) == INVALID
+    assert call(t2f=None) == INVALID
+    assert call(ids=None) == INVALID
+    assert call(ws=None) == WORKSPACE
+    assert call(ws_n=n - 1) == WORKSPACE
