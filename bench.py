@@ -211,6 +211,20 @@ def main():
     ms_warm = time_calls(warm, args.steps, torch) / args.steps
     log(f"warm: {ms_warm * 1000:.2f} us/step; single launches bracketed by events: {us_launch:.2f} us")
 
+    # the pages' own draft step: one multinomial draw per row (Gumbel-max),
+    # cold, a new offset per call
+    s_ids = torch.empty(M, dtype=torch.int32, device=dev)
+    s_p = torch.empty(M, dtype=torch.float32, device=dev)
+    ws_s = torch.zeros(dlh.vt_draft_head_workspace_size(M, V_high, d, 1), dtype=torch.uint8,
+                       device=dev)
+
+    def cold_sample(i):
+        dlh.vt_draft_sample(h, copies[i % R], t2f, 2024, i, full_ids=s_ids, probs=s_p, ws=ws_s)
+    for i in range(50):
+        cold_sample(i)
+    ms_sample = time_calls(cold_sample, args.steps, torch) / args.steps
+    log(f"sample (cold): {ms_sample * 1000:.2f} us/step")
+
     # pipeline: one pass of every step (count, select, gather, draft head)
     def pipeline():
         dlh.vt_count_freq(ids, w.V, counts=counts, n_invalid=n_inv)
@@ -277,12 +291,17 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic() if (w.name == "llama3_8b" and M == 1) else None,
-                     "kernel": "head_gemv_kernel", "bytes_per_launch": nb,
+                     "kernel": "head_gemv_kernel" if M <= 4 else
+                               "h_pack_kernel + head_mfma_kernel + head_merge_kernel",
+                     "bytes_per_launch": nb,
                      "us_per_launch": round(ms_step * 1000, 3),
                      "us_single_launch_events": round(us_launch, 3)},
         "cpu_baseline": cpu,
         "warm": {"us_per_call": round(ms_warm * 1000, 3),
                  "GB_per_s": round(nb / (ms_warm * 1e-3) / 1e9, 1)},
+        "sample": {"us_per_call": round(ms_sample * 1000, 3),
+                   "GB_per_s": round(head_bytes(V_high, d, M, 1) / (ms_sample * 1e-3) / 1e9, 1),
+                   "what": "vt_draft_sample: one multinomial draw per row (Gumbel-max), cold"},
         "untrimmed": {"V_high": w.V, "us_per_call": round(us_untrim, 3),
                       "trim_speedup": round(us_untrim / (ms_step * 1000), 3)},
         "prep": {"count_us": round(us_count, 2),
