@@ -337,15 +337,20 @@ __device__ void final_merge(const HeadArgs &a, int m, MergeShared<WAVES> &sh) {
   for (int w = 1; w < WAVES; ++w) S += sh.f[w];
   uint64_t key = 0;  // rank `tid` for tid < k
   if (found <= (uint32_t)kWave) {
-    if (tid < kWave) {
-      sh.sc[0][tid] = tid < (int)found ? sh.cand[tid] : 0ull;
-      sh.sc[1][tid] = 0;
+    // Wave 0 ranks the few survivors against each other (a loop over the
+    // survivors only) and writes each one to its output slot; at least k
+    // keys survive because T is at most the k-th largest key.
+    if (wave == 0) {
+      const uint64_t v = lane < (int)found ? sh.cand[lane] : 0ull;
+      uint32_t r = 0;
+      for (uint32_t j = 0; j < found; ++j) r += sh.cand[j] > v;
+      if (lane < (int)found && r < (uint32_t)k) {
+        a.full_ids[(size_t)m * k + r] = key_id(v);
+        a.probs[(size_t)m * k + r] = __expf(key_logit(v) - mu) / S;
+      }
     }
-    __syncthreads();
-    const uint32_t r = block_rank<WAVES, 1>(sh.sc[0], &sh.prank[0][0][0]);
-    if (wave == 0 && r < (uint32_t)k) sh.sc[1][r] = sh.sc[0][lane];
-    __syncthreads();
-    if (tid < kWave) key = sh.sc[1][tid];
+    __syncthreads();  // sh is reused by the next draft row's merge
+    return;
   } else if (found <= (uint32_t)kCandCap) {
     block_sort_desc<WAVES>(sh.cand, found);
     if (wave == 0) key = sh.cand[lane];

@@ -149,7 +149,9 @@ int vt_gather_head(const uint16_t *W, int32_t V, int32_t d,
  * d         d % 8 == 0, 8 <= d <= VT_D_MAX
  * W_trim    device, bf16[V_high, d], 16-byte aligned; 1 <= V_high <= VT_VHIGH_MAX
  * t2f       device, int32[V_high]; only copied to the output and used to
- *           break ties, never used as an address
+ *           break ties, never used as an address. Its entries must be
+ *           distinct (vt_select_vocab makes them so); with a repeated id
+ *           and equal logits some output slots are left unwritten.
  * k         1 <= k <= min(V_high, VT_K_MAX)
  * full_ids  device, int32[M, k];  probs  device, float[M, k]
  * ws        device workspace of vt_draft_head_workspace_size(M, V_high, d, k)
