@@ -59,9 +59,11 @@ def _load():
             lib.or_gumbel.restype = C.c_double
             lib.or_gumbel_block.argtypes = [u64, u64, i32, i32, P]
             lib.or_gumbel_block.restype = C.c_int
+            lib.or_coverage_curve.argtypes = [P, i32, P, i32, C.c_double, P, P, P]
             lib.or_threads.argtypes = []
             for f in (lib.or_threads, lib.or_count, lib.or_select, lib.or_gather, lib.or_logits,
-                      lib.or_softmax, lib.or_topk, lib.or_draft_head, lib.or_draft_sample):
+                      lib.or_softmax, lib.or_topk, lib.or_draft_head, lib.or_draft_sample,
+                      lib.or_coverage_curve):
                 f.restype = C.c_int
             _lib = lib
     return _lib
@@ -235,3 +237,19 @@ def draft_sample(h, W_trim, t2f, seed: int, offset: int, want_logits: bool = Fal
     if want_logits:
         return ids, probs, ti, z
     return ids, probs, ti
+
+
+def coverage_curve(counts, order, min_coverage: float = 1.0):
+    """Cumulative counts along a ranking (VocabTrim page, Step 2's coverage
+    for every V_high; the guidance table's coverage threshold).
+
+    Returns ``(cum uint64[L], tot, v_high)``; coverage at n is cum[n-1]/tot.
+    """
+    c = _arr(counts, np.uint32, 1)
+    o = _arr(order, np.int32, 1)
+    cum = np.empty(o.size, np.uint64)
+    tot = np.zeros(1, np.uint64)
+    vh = np.zeros(1, np.int32)
+    _ok(_load().or_coverage_curve(_p(c), c.size, _p(o), o.size, C.c_double(min_coverage),
+                                  _p(cum), _p(tot), _p(vh)), "coverage_curve")
+    return cum, int(tot[0]), int(vh[0])

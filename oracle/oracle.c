@@ -416,3 +416,40 @@ done:
     free(S);
     return rc;
 }
+
+/* Coverage of every prefix of a ranking ([VT] Step 2's coverage, the
+ * fraction of counted tokens the kept ids cover, for every V_high at once;
+ * the guidance table's coverage threshold then picks V_high; with counts of
+ * an evaluation stream it is Step 5's share of tokens inside the trimmed
+ * vocabulary, one minus the miss rate):
+ *   cum[i]  = sum_{r <= i} counts[order[r]]   for i < L (ids outside [0, V)
+ *             count as 0)
+ *   tot     = sum_{v < V} counts[v]
+ *   v_high  = smallest n in [1, L] with (double)cum[n-1] >= min_coverage *
+ *             (double)tot, or -1 if there is none (v_high may be NULL).
+ * Coverage at n is cum[n-1] / tot. */
+int or_coverage_curve(const uint32_t *counts, int32_t V, const int32_t *order,
+                      int32_t L, double min_coverage, uint64_t *cum,
+                      uint64_t *tot, int32_t *v_high)
+{
+    if (!counts || !order || !cum || !tot || V <= 0 || L <= 0 || L > V)
+        return OR_BAD;
+    uint64_t t = 0;
+    for (int32_t v = 0; v < V; ++v)
+        t += counts[v];
+    *tot = t;
+    const double x = min_coverage * (double)t;
+    uint64_t c = 0;
+    int32_t n = -1;
+    for (int32_t i = 0; i < L; ++i) {
+        const int32_t id = order[i];
+        if (id >= 0 && id < V)
+            c += counts[id];
+        cum[i] = c;
+        if (n < 0 && (double)c >= x)
+            n = i + 1;
+    }
+    if (v_high)
+        *v_high = n;
+    return OR_OK;
+}
