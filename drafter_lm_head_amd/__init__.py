@@ -28,7 +28,7 @@ __all__ = [
     "VT_VHIGH_MAX", "vt_count_freq", "vt_select_vocab", "vt_gather_head",
     "vt_draft_head", "vt_draft_sample", "vt_head_logits", "vt_count_freq_workspace_size",
     "vt_select_vocab_workspace_size", "vt_draft_head_workspace_size",
-    "coverage",
+    "coverage", "vt_coverage_curve", "vt_coverage_curve_workspace_size",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -53,6 +53,8 @@ _SIGS = {
     "vt_draft_head": (_INT, [_P, _I32, _I32, _P, _I32, _P, _I32, _P, _P, _P, _SZ, _P]),
     "vt_draft_sample": (_INT, [_P, _I32, _I32, _P, _I32, _P, _U64, _U64, _P, _P, _P, _SZ, _P]),
     "vt_head_logits": (_INT, [_P, _I32, _I32, _P, _I32, _P, _P]),
+    "vt_coverage_curve_workspace_size": (_SZ, [_I32, _I32]),
+    "vt_coverage_curve": (_INT, [_P, _I32, _P, _I32, C.c_double, _P, _P, _P, _P, _SZ, _P]),
 }
 
 
@@ -280,3 +282,28 @@ def vt_head_logits(h: torch.Tensor, W_trim: torch.Tensor,
     _check(lib().vt_head_logits(_ptr(h), M, d, _ptr(W_trim), V_high, _ptr(out), _stream(h)),
            "vt_head_logits")
     return out
+
+
+def vt_coverage_curve_workspace_size(V: int, L: int) -> int:
+    return int(lib().vt_coverage_curve_workspace_size(V, L))
+
+
+def vt_coverage_curve(counts: torch.Tensor, order: torch.Tensor, min_coverage: float = 1.0):
+    """Cumulative counts along a ranking and the smallest prefix reaching a
+    coverage threshold (VocabTrim Step 2 coverage for every V_high; guidance
+    table threshold): (cum uint64[L], tot_sum uint64[1], v_high int32[1])."""
+    _dev(counts, "counts", (torch.uint32, torch.int32), 1)
+    _dev(order, "order", (torch.int32,), 1)
+    V, L = counts.numel(), order.numel()
+    dev = counts.device
+    cum = torch.empty(L, dtype=torch.int64, device=dev).view(torch.uint64)
+    tot = torch.empty(1, dtype=torch.int64, device=dev).view(torch.uint64)
+    vh = torch.empty(1, dtype=torch.int32, device=dev)
+    need = vt_coverage_curve_workspace_size(V, L)
+    if need == 0:
+        raise ValueError("need 1 <= len(order) <= len(counts)")
+    ws = _workspace(dev, "coverage", need, False)
+    _check(lib().vt_coverage_curve(_ptr(counts), V, _ptr(order), L, float(min_coverage),
+                                   _ptr(cum), _ptr(tot), _ptr(vh), _ptr(ws), ws.numel(),
+                                   _stream(counts)), "vt_coverage_curve")
+    return cum, tot, vh

@@ -83,6 +83,24 @@ int vt_select_vocab(const uint32_t *counts, int32_t V, int32_t V_high,
                                       tot_sum, ws, as_stream(stream)));
 }
 
+// --------------------------------------------------------- coverage curve
+size_t vt_coverage_curve_workspace_size(int32_t V, int32_t L) {
+  if (V <= 0 || L <= 0 || L > V) return 0;
+  return vt::coverage_ws_bytes(V, L);
+}
+
+int vt_coverage_curve(const uint32_t *counts, int32_t V, const int32_t *order,
+                      int32_t L, double min_coverage, uint64_t *cum,
+                      uint64_t *tot_sum, int32_t *v_high, void *ws,
+                      size_t ws_bytes, void *stream) {
+  if (!counts || !order || !cum || !tot_sum) return VT_ERR_INVALID_ARG;
+  if (V <= 0 || L <= 0 || L > V) return VT_ERR_INVALID_ARG;
+  if (!ws || !aligned(ws, 256) || ws_bytes < vt_coverage_curve_workspace_size(V, L))
+    return VT_ERR_WORKSPACE;
+  return hip_status(vt::launch_coverage(counts, V, order, L, min_coverage, cum,
+                                        tot_sum, v_high, ws, as_stream(stream)));
+}
+
 // ----------------------------------------------------------------- gather
 int vt_gather_head(const uint16_t *W, int32_t V, int32_t d,
                    const int32_t *t2f, int32_t V_high, uint16_t *W_trim,

@@ -52,6 +52,12 @@ hipError_t launch_draft_sample(const uint16_t *h, int32_t M, int32_t d,
                                const uint16_t *W_trim, int32_t V_high, const int32_t *t2f,
                                uint64_t seed, uint64_t offset, int32_t *full_ids,
                                float *probs, void *ws, hipStream_t stream);
+// Coverage curve of a ranking.
+size_t coverage_ws_bytes(int32_t V, int32_t L);
+hipError_t launch_coverage(const uint32_t *counts, int32_t V, const int32_t *order, int32_t L,
+                           double min_coverage, uint64_t *cum, uint64_t *tot_sum,
+                           int32_t *v_high, void *ws, hipStream_t stream);
+
 hipError_t launch_head_logits(const uint16_t *h, int32_t M, int32_t d,
                               const uint16_t *W_trim, int32_t V_high,
                               float *logits, hipStream_t stream);

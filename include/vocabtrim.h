@@ -113,6 +113,33 @@ int vt_select_vocab(const uint32_t *counts, int32_t V, int32_t V_high,
                     uint64_t *tot_sum, void *ws, size_t ws_bytes,
                     void *stream);
 
+/* --------------------------------------------------------- coverage curve
+ * Coverage of every prefix of a ranking: [VT] Step 2's coverage (the share
+ * of counted tokens the kept ids cover) for every V_high at once, and the
+ * smallest V_high that reaches a coverage threshold (the guidance table
+ * recommends 85-95 %). Given an evaluation stream's counts and the
+ * calibration ranking, 1 - coverage is [VT] Step 5's share of tokens that
+ * fall outside the trimmed vocabulary.
+ *
+ *   cum[i]  = sum_{r <= i} counts[order[r]]   (i < L; ids outside [0, V) add 0)
+ *   tot_sum = sum_{v < V} counts[v]
+ *   v_high  = smallest n in [1, L] with (double)cum[n - 1] >= min_coverage *
+ *             (double)tot_sum, or -1 if none (e.g. min_coverage > 1)
+ * Coverage at n is cum[n - 1] / tot_sum (tot_sum == 0: no token counted).
+ *
+ * counts  device, uint32[V];  order  device, int32[L], 1 <= L <= V, e.g. the
+ *         t2f of vt_select_vocab with V_high = L
+ * cum     device, uint64[L];  tot_sum  device, uint64[1]
+ * v_high  device, int32[1], or NULL to skip it
+ * ws      device workspace of vt_coverage_curve_workspace_size(V, L) bytes,
+ *         256-byte aligned; no initial contents required.
+ * The sums are exact integers; the threshold test is taken in double. */
+size_t vt_coverage_curve_workspace_size(int32_t V, int32_t L);
+int vt_coverage_curve(const uint32_t *counts, int32_t V, const int32_t *order,
+                      int32_t L, double min_coverage, uint64_t *cum,
+                      uint64_t *tot_sum, int32_t *v_high, void *ws,
+                      size_t ws_bytes, void *stream);
+
 /* ----------------------------------------------------------------- gather
  * Trimmed head: [VT] Step 3 keeps the head rows of the kept ids; [FR] key
  * design shrinks the head from d x 128k to d x 32k.

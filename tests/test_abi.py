@@ -178,3 +178,18 @@ def test_draft_sample_validation(lib):
     assert call(ids=None) == INVALID
     assert call(ws=None) == WORKSPACE
     assert call(ws_n=n - 1) == WORKSPACE
+
+
+def test_coverage_curve_validation(lib):
+    assert lib.vt_coverage_curve_workspace_size(0, 1) == 0
+    assert lib.vt_coverage_curve_workspace_size(10, 11) == 0
+    n = lib.vt_coverage_curve_workspace_size(100000, 50000)
+    assert n > 0
+    f = lib.vt_coverage_curve
+    assert f(None, 100, A, 10, 0.9, A, A, None, A, n, None) == INVALID
+    assert f(A, 100, None, 10, 0.9, A, A, None, A, n, None) == INVALID
+    assert f(A, 100, A, 101, 0.9, A, A, None, A, n, None) == INVALID
+    assert f(A, 100, A, 10, 0.9, None, A, None, A, n, None) == INVALID
+    assert f(A, 100, A, 10, 0.9, A, None, None, A, n, None) == INVALID
+    assert f(A, 100000, A, 50000, 0.9, A, A, None, None, n, None) == WORKSPACE
+    assert f(A, 100000, A, 50000, 0.9, A, A, None, A, n - 1, None) == WORKSPACE
