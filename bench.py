@@ -162,6 +162,10 @@ def main():
     us_count = median_us(lambda: dlh.vt_count_freq(ids, w.V, counts=counts, n_invalid=n_inv), reps, torch)
     us_select = median_us(lambda: dlh.vt_select_vocab(counts, w.V_high), reps, torch)
     us_gather = median_us(lambda: dlh.vt_gather_head(W, t2f, out=Wt), reps, torch)
+    order_full, _, _, _ = dlh.vt_select_vocab(counts, w.V)
+    us_cov = median_us(lambda: dlh.vt_coverage_curve(counts, order_full, 0.9), reps, torch)
+    _, _, vh90 = dlh.vt_coverage_curve(counts, order_full, 0.9)
+    v_high_90 = int(vh90.item())
     log(f"prep: count {us_count:.1f} us, select {us_select:.1f} us, gather {us_gather:.1f} us, "
         f"coverage {cov:.4f}")
 
@@ -309,7 +313,9 @@ def main():
                  "select_us": round(us_select, 2),
                  "gather_us": round(us_gather, 2),
                  "gather_GB_per_s": round(prep_bytes_gather / (us_gather * 1e-6) / 1e9, 1),
-                 "coverage": round(cov, 6)},
+                 "coverage": round(cov, 6),
+                 "coverage_curve_us": round(us_cov, 2),
+                 "v_high_for_90pct": v_high_90},
         "pipeline_us": round(us_pipe, 2),
     }
     if sweep is not None:
