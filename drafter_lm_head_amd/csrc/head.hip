@@ -380,25 +380,14 @@ __device__ void final_merge(const HeadArgs &a, int m, MergeShared<WAVES> &sh) {
   __syncthreads();
 }
 
-// One row per wave and step: the W loads of a step (CPL 16-byte chunks per
-// lane) are all in flight at once, and 16 waves per workgroup keep enough
-// rows in flight per CU.
-template <int MT, int CPL>
-constexpr int rows_per_step() { return 1; }
-
-// Waves per workgroup: VT_GEMV_WAVES while h and one row fit the VGPRs
-// that many waves allow (128 at 16 waves), else 8.
-#ifndef VT_GEMV_WAVES
-#define VT_GEMV_WAVES 8
-#endif
-template <int MT, int CPL>
-constexpr int gemv_waves() {
-  return (VT_GEMV_WAVES <= 8 || (1 + MT) * CPL * 4 <= 96) ? VT_GEMV_WAVES : 8;
-}
+// GEMV workgroups: 8 waves, one row per wave and step; the W loads of a
+// step (CPL 16-byte chunks per lane) are all in flight at once, and two
+// workgroups per CU (16 waves) keep enough rows in flight.
+constexpr int kGemvWaves = 8;
 
 template <int WAVES, int MT, int CPL, bool RAGGED, bool LOGITS>
 __global__ __launch_bounds__(WAVES *kWave) void head_gemv_kernel(HeadArgs a) {
-  constexpr int U = rows_per_step<MT, CPL>();
+  constexpr int U = 1;  // rows per wave and step
   static_assert(kTileRows % (WAVES * U) == 0, "tile must split evenly");
   static_assert(MT <= WAVES, "one wave per draft row in the epilogue");
   __shared__ float s_z[MT][kTileRows];
@@ -728,7 +717,7 @@ constexpr int kCplSet[] = {1, 2, 3, 4, 5, 6, 7, 8, 12, 16};
 
 template <int MT, bool LOGITS, int CPL, bool RAGGED>
 hipError_t launch_one(const HeadArgs &a, hipStream_t stream) {
-  constexpr int WAVES = gemv_waves<MT, CPL>();
+  constexpr int WAVES = kGemvWaves;
   hipLaunchKernelGGL((head_gemv_kernel<WAVES, MT, CPL, RAGGED, LOGITS>),
                      dim3(a.tiles), dim3(WAVES * kWave), 0, stream, a);
   return hipGetLastError();

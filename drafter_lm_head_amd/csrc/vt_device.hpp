@@ -1,6 +1,6 @@
 // Device helpers shared by the gfx950 kernels: wave64 reductions on DPP,
-// order-preserving 64-bit top-k keys, bitonic sort across a wave, and the
-// hand-off of partial results between workgroups.
+// order-preserving 64-bit top-k keys, the counter-based generator of the
+// multinomial draw, and the hand-off of partial results between workgroups.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -169,23 +169,6 @@ __device__ __forceinline__ float gumbel(uint32_t seed_lo, uint32_t seed_hi, uint
   const uint32_t x = philox_word0((uint32_t)j, (uint32_t)m, off_lo, off_hi, seed_lo, seed_hi);
   const float u = ((float)(x >> 8) + 0.5f) * 0x1p-24f;
   return -logf(-logf(u));
-}
-
-// Sorts one key per lane so that lane 0 holds the largest (bitonic network).
-__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key) {
-  const int lane = __lane_id();
-#pragma unroll
-  for (int size = 2; size <= kWave; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      uint64_t other = __shfl_xor(key, stride);
-      const bool lower = (lane & stride) == 0;
-      const bool desc = (lane & size) == 0;
-      key = (lower == desc) ? max_u64(key, other)
-                            : (key < other ? key : other);
-    }
-  }
-  return key;
 }
 
 // -------------------------------------------------- cross-workgroup order
