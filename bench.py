@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E peak, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak, TFLOP/s
 METRIC = "draft-head calls/s & µs/call (d=4096,V_high=32k,M=1); % of peak HBM GB/s"
 
 
@@ -318,6 +319,18 @@ def main():
                  "v_high_for_90pct": v_high_90},
         "pipeline_us": round(us_pipe, 2),
     }
+    if M > 4:
+        # The wide-tree path is a dense bf16 contraction on the matrix cores: report its
+        # rate against the dense bf16 peak. M is padded to whole 16-row MFMA tiles.
+        fl = 2.0 * M * V_high * d
+        fl_issued = 2.0 * (-(-M // 16) * 16) * V_high * d
+        out["mfma"] = {"useful_TFLOP_per_s": round(fl / (ms_step * 1e-3) / 1e12, 1),
+                       "issued_TFLOP_per_s": round(fl_issued / (ms_step * 1e-3) / 1e12, 1),
+                       "peak_TFLOP_per_s": MFMA_BF16_PEAK_TFLOPS,
+                       "frac": round(fl / (ms_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                       "flops_per_byte": round(fl / nb, 2),
+                       "ridge_flops_per_byte": round(MFMA_BF16_PEAK_TFLOPS / (HBM_PEAK_GBS / 1000), 1),
+                       "over": "the whole call (pack + contraction + merge)"}
     if sweep is not None:
         out["sweep"] = sweep
     print(json.dumps(out), flush=True)
