@@ -45,6 +45,8 @@ struct HeadArgs {
   int32_t sample;
   uint32_t seed_lo, seed_hi, off_lo, off_hi;
   uint64_t *tile_z;      // [M][tiles]: bits of z of each tile's drawn row
+  float *zbuf;           // MFMA path, top-k mode: logits [M][zpitch]
+  int32_t zpitch;        // tiles * kTileRows floats
 };
 
 __device__ __forceinline__ uint64_t pack_ms(float mu, float S) {
@@ -93,6 +95,7 @@ struct alignas(16) MergeShared {
   unsigned long long kmax, T;
   uint32_t cnt;
   float f[WAVES], f2[WAVES], zw[WAVES];
+  uint32_t gm[kWave];                        // group maxima (row merge)
 };
 
 // Ranks (0 = largest) of NR rows of 64 keys in LDS, keys[r * 64 + lane],
@@ -521,48 +524,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMfmaWaves = 4;
 
-// One wave publishes one draft row's tile partial: lane j holds the key of
-// tile row j (0 past V_high) and its logit z. The tile's top-k come from
-// rank counting over LDS broadcasts; sc and top are 64-key LDS buffers of
-// this wave (16-byte aligned).
-__device__ __forceinline__ void wave_publish_tile(const HeadArgs &a, int m, int tile,
-                                                  uint64_t key, float z, bool valid,
-                                                  uint64_t *sc, uint64_t *top) {
-  typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
-  const int lane = __lane_id(), k = a.k;
-  sc[lane] = key;
-  top[lane] = 0;
-  __builtin_amdgcn_wave_barrier();
-  // Rank by counting larger keys: 32 broadcast reads, issued in two batches
-  // of 16 so that their LDS latencies overlap.
-  uint32_t rank = 0;
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    u64x2 q[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) q[j] = *reinterpret_cast<const u64x2 *>(sc + half * 32 + 2 * j);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) rank += (q[j].x > key) + (q[j].y > key);
-  }
-  if (rank < (uint32_t)k) top[rank] = key;
-  __builtin_amdgcn_wave_barrier();
-  const uint64_t tk = top[lane];
-  const uint64_t head = top[0], kth = top[k - 1];
-  const float mu = key_logit(head);
-  const float S = wave_sum(valid ? __expf(z - mu) : 0.f);
-  if (lane < k) publish_u64(a.tile_keys + ((size_t)m * a.tiles + tile) * k + lane, tk);
-  if (lane == 0) {
-    publish_u64(a.tile_ms + (size_t)m * a.tiles + tile, pack_ms(mu, S));
-    const int grp = tile / a.tiles_per_group;
-    __hip_atomic_fetch_max(a.group_max + (size_t)m * kGroups + grp, head,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_fetch_max(a.group_kth + (size_t)m * kGroups + grp, kth,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __builtin_amdgcn_wave_barrier();
-}
-
 // W is staged through wave-private LDS: the operand layout (16 rows x 64
 // bytes per load) is slow to fetch from HBM directly, so each load
 // instruction instead reads 4 rows x 256 contiguous bytes; rows are padded
@@ -590,7 +551,6 @@ __global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a
     float part[kMfmaWaves][NT * 16][kPartPitch];
   };
   __shared__ Smem sm;
-  __shared__ alignas(16) uint64_t s_sc[kMfmaWaves][2][kWave];
   const int lane = __lane_id(), wave = threadIdx.x / kWave;
   const int tile = blockIdx.x, row0 = tile * kTileRows;
   const int c16 = a.c16, M = a.M;
@@ -664,6 +624,8 @@ __global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a
     for (int cb = 0; cb < NT; ++cb)
       *reinterpret_cast<f32x4 *>(&sm.part[wave][cb * 16 + r16][rb * 16 + 4 * g]) = acc[rb][cb];
   __syncthreads();
+  // Top-k mode: the sums go straight to the logit buffer, which the row
+  // merge reads; sampling mode keeps them in LDS for the tile epilogue.
   for (int i = threadIdx.x; i < NT * 16 * (kTileRows / 4); i += kMfmaWaves * kWave) {
     const int row = i / (kTileRows / 4), c4 = 4 * (i % (kTileRows / 4));
     f32x4 val = *reinterpret_cast<const f32x4 *>(&sm.part[0][row][c4]);
@@ -671,30 +633,214 @@ __global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a
     for (int w = 1; w < kMfmaWaves; ++w)
       val += *reinterpret_cast<const f32x4 *>(&sm.part[w][row][c4]);
     *reinterpret_cast<f32x4 *>(&sm.part[0][row][c4]) = val;
+    if (!a.sample && row < M)
+      *reinterpret_cast<f32x4 *>(a.zbuf + (size_t)row * a.zpitch + row0 + c4) = val;
   }
   __syncthreads();
+  if (!a.sample) {
+    // Softmax partial of each draft row over the tile, one lane per draft row:
+    // wave q takes tile rows 16 q .. 16 q + 15, then wave 0 combines the four
+    // quarters in a fixed order and publishes (max, sum of exp(z - max)).
+    const int m = lane, q = wave;
+    float mq = -INFINITY, sq = 0.f;
+    if (m < M) {
+      float zq[16];
+#pragma unroll
+      for (int i = 0; i < 16; i += 4)
+        *reinterpret_cast<f32x4 *>(&zq[i]) =
+            *reinterpret_cast<const f32x4 *>(&sm.part[0][m][16 * q + i]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (row0 + 16 * q + i < a.V_high) mq = fmaxf(mq, zq[i]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (row0 + 16 * q + i < a.V_high) sq += __expf(zq[i] - mq);
+    }
+    __syncthreads();  // every quarter has read part[0] before it is reused
+    float *qm = &sm.part[1][0][0], *qs = &sm.part[2][0][0];
+    qm[q * kWave + lane] = mq;
+    qs[q * kWave + lane] = sq;
+    __syncthreads();
+    if (wave == 0 && m < M) {
+      float mu = qm[lane];
+#pragma unroll
+      for (int w = 1; w < kMfmaWaves; ++w) mu = fmaxf(mu, qm[w * kWave + lane]);
+      float S = 0.f;
+#pragma unroll
+      for (int w = 0; w < kMfmaWaves; ++w) {
+        const float mw = qm[w * kWave + lane];
+        if (mw != -INFINITY) S += qs[w * kWave + lane] * __expf(mw - mu);
+      }
+      a.tile_ms[(size_t)m * a.tiles + tile] = pack_ms(mu, S);
+    }
+    return;
+  }
 
   const bool valid = row0 + lane < a.V_high;
   const int32_t fid = valid ? a.t2f[row0 + lane] : 0;
-  for (int m = wave; m < M; m += kMfmaWaves) {
-    const float z = sm.part[0][m][lane];
-    if (a.sample) {
-      wave_publish_sample(a, m, tile, row0, z, fid, valid);
-      continue;
+  for (int m = wave; m < M; m += kMfmaWaves)
+    wave_publish_sample(a, m, tile, row0, sm.part[0][m][lane], fid, valid);
+}
+
+// Top-k merge of the MFMA path, one workgroup per draft row m, from the
+// tiles' softmax partials and the logits in the workspace:
+//   * the softmax max and sum over the row come from the tile partials,
+//     combined in a fixed order;
+//   * each tile's max is a logit of that tile, so the k-th largest of the
+//     maxima of 64 disjoint groups of tiles (with multiplicity) is at most
+//     the row's k-th largest logit: only tiles whose max reaches it can hold
+//     a pick, typically k to 2k of them;
+//   * the logits of those tiles at or above the bound become keys in LDS
+//     and are ranked as in the tile merge.
+constexpr int kTreeWaves = 8;
+
+template <int WAVES>
+__global__ __launch_bounds__(WAVES *kWave) void tree_merge_kernel(HeadArgs a) {
+  constexpr int NT = WAVES * kWave;
+  constexpr int kTpt = (kMaxTiles + NT - 1) / NT;  // tiles per thread
+  constexpr int GS = NT / kWave;                   // threads per tile group
+  static_assert((GS & (GS - 1)) == 0 && GS <= kWave, "group of threads within a wave");
+  __shared__ MergeShared<WAVES> sh;
+  __shared__ int32_t s_tiles[kMaxTiles];
+  __shared__ uint32_t s_ntiles;
+  const int m = blockIdx.x, tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
+  const int k = a.k, V = a.V_high, tiles = a.tiles;
+  const uint64_t *ms = a.tile_ms + (size_t)m * tiles;
+  const float *zr = a.zbuf + (size_t)m * a.zpitch;
+
+  uint64_t mst[kTpt];
+#pragma unroll
+  for (int j = 0; j < kTpt; ++j) {
+    const int t = tid + j * NT;
+    mst[j] = t < tiles ? ms[t] : 0ull;
+  }
+  float mu_l = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kTpt; ++j)
+    if (tid + j * NT < tiles) mu_l = fmaxf(mu_l, ms_max(mst[j]));
+  uint32_t gmx = mu_l == -INFINITY ? 0u : ord_from_f32(mu_l);
+#pragma unroll
+  for (int x = 1; x < GS; x <<= 1) gmx = max(gmx, (uint32_t)__shfl_xor((int)gmx, x));
+  if ((lane & (GS - 1)) == 0) sh.gm[tid / GS] = gmx;
+  const float mw = wave_max(mu_l);
+  if (lane == 0) sh.f[wave] = mw;
+  if (tid == 0) {
+    sh.cnt = 0;
+    s_ntiles = 0;
+  }
+  __syncthreads();
+  float mu = sh.f[0];
+  for (int w = 1; w < WAVES; ++w) mu = fmaxf(mu, sh.f[w]);
+  float s_l = 0.f;
+#pragma unroll
+  for (int j = 0; j < kTpt; ++j)
+    if (tid + j * NT < tiles) s_l += ms_sum(mst[j]) * __expf(ms_max(mst[j]) - mu);
+  const float sw = wave_sum(s_l);
+  if (lane == 0) sh.f2[wave] = sw;
+  if (wave == 0) {
+    // k-th largest of the 64 group maxima: count the larger and the
+    // not-smaller ones with broadcast reads of all 64.
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+    const uint32_t gv = sh.gm[lane];
+    u32x4v q[kWave / 4];
+#pragma unroll
+    for (int j = 0; j < kWave / 4; ++j) q[j] = *reinterpret_cast<const u32x4v *>(&sh.gm[4 * j]);
+    uint32_t gt = 0, ge = 0;
+#pragma unroll
+    for (int j = 0; j < kWave / 4; ++j)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        gt += q[j][c] > gv;
+        ge += q[j][c] >= gv;
+      }
+    const uint64_t hit = __ballot(gt < (uint32_t)k && ge >= (uint32_t)k);
+    if (lane == 0)
+      sh.T = hit ? (uint32_t)__builtin_amdgcn_readlane((int)gv, __builtin_ctzll(hit)) : 0u;
+  }
+  __syncthreads();
+  const uint32_t T = (uint32_t)sh.T;
+  float S = sh.f2[0];
+  for (int w = 1; w < WAVES; ++w) S += sh.f2[w];
+#pragma unroll
+  for (int j = 0; j < kTpt; ++j) {
+    const int t = tid + j * NT;
+    if (t < tiles && ord_from_f32(ms_max(mst[j])) >= T) s_tiles[atomicAdd(&s_ntiles, 1u)] = t;
+  }
+  __syncthreads();
+  const int ne = (int)s_ntiles * kTileRows;  // candidate logits
+  constexpr int kRound = 4;
+  for (int base = 0; base < ne; base += kRound * NT) {
+    float zv[kRound];
+    int jv[kRound];
+#pragma unroll
+    for (int i = 0; i < kRound; ++i) {
+      const int e = base + i * NT + tid;
+      jv[i] = e < ne ? s_tiles[e / kTileRows] * kTileRows + e % kTileRows : V;
+      zv[i] = jv[i] < V ? zr[jv[i]] : 0.f;
     }
-    wave_publish_tile(a, m, tile, valid ? make_key(z, fid) : 0ull, z, valid,
-                      s_sc[wave][0], s_sc[wave][1]);
+#pragma unroll
+    for (int i = 0; i < kRound; ++i)
+      if (jv[i] < V && ord_from_f32(zv[i]) >= T) {
+        const uint32_t pos = atomicAdd(&sh.cnt, 1u);
+        if (pos < (uint32_t)kCandCap) sh.cand[pos] = make_key(zv[i], a.t2f[jv[i]]);
+      }
+  }
+  __syncthreads();
+  const uint32_t found = sh.cnt;
+  uint64_t key = 0;  // rank `tid` for tid < k
+  if (found <= (uint32_t)kWave) {
+    if (wave == 0) {
+      const uint64_t x = lane < (int)found ? sh.cand[lane] : 0ull;
+      uint32_t r = 0;
+      for (uint32_t j = 0; j < found; ++j) r += sh.cand[j] > x;
+      if (lane < (int)found && r < (uint32_t)k) {
+        a.full_ids[(size_t)m * k + r] = key_id(x);
+        a.probs[(size_t)m * k + r] = __expf(key_logit(x) - mu) / S;
+      }
+    }
+    return;
+  } else if (found <= (uint32_t)kCandCap) {
+    block_sort_desc<WAVES>(sh.cand, found);
+    if (tid < k) key = sh.cand[tid];
+  } else {
+    // Massive exact ties: k rounds of "largest key below the previous one"
+    // over the candidate logits.
+    uint64_t prev = ~0ull;
+    for (int r = 0; r < k; ++r) {
+      uint64_t best = 0;
+      for (int e = tid; e < ne; e += NT) {
+        const int j = s_tiles[e / kTileRows] * kTileRows + e % kTileRows;
+        if (j < V) {
+          const float z = zr[j];
+          if (ord_from_f32(z) >= T) {
+            const uint64_t kv = make_key(z, a.t2f[j]);
+            if (kv < prev) best = max_u64(best, kv);
+          }
+        }
+      }
+      best = wave_max_u64(best);
+      __syncthreads();
+      if (tid == 0) sh.kmax = 0;
+      __syncthreads();
+      if (lane == 0) atomicMax(&sh.kmax, (unsigned long long)best);
+      __syncthreads();
+      best = sh.kmax;
+      if (tid == r) key = best;
+      prev = best;
+    }
+  }
+  if (tid < k) {
+    a.full_ids[(size_t)m * k + tid] = key_id(key);
+    a.probs[(size_t)m * k + tid] = __expf(key_logit(key) - mu) / S;
   }
 }
 
-// One workgroup per draft row merges the published tile partials.
+// Sampling mode: one workgroup per draft row merges the published tile
+// partials.
 template <int WAVES>
 __global__ __launch_bounds__(WAVES *kWave) void head_merge_kernel(HeadArgs a) {
   __shared__ MergeShared<WAVES> sh;
-  if (a.sample)
-    sample_merge<WAVES>(a, blockIdx.x, sh);
-  else
-    final_merge<WAVES>(a, blockIdx.x, sh);
+  sample_merge<WAVES>(a, blockIdx.x, sh);
 }
 
 template <int NT>
@@ -708,7 +854,11 @@ hipError_t launch_mfma(const HeadArgs &a, hipStream_t stream) {
                      stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((head_merge_kernel<8>), dim3(a.M), dim3(8 * kWave), 0, stream, a);
+  if (a.sample)
+    hipLaunchKernelGGL((head_merge_kernel<8>), dim3(a.M), dim3(8 * kWave), 0, stream, a);
+  else
+    hipLaunchKernelGGL((tree_merge_kernel<kTreeWaves>), dim3(a.M), dim3(kTreeWaves * kWave), 0,
+                       stream, a);
   return hipGetLastError();
 }
 
@@ -759,14 +909,19 @@ HeadPlan head_plan(int32_t M, int32_t V_high, int32_t k) {
   p.off_group = off;
   off += (size_t)VT_M_MAX * 2 * kGroups * 8;
   p.zero_bytes = off;
+  // Tile keys: k per tile on the GEMV path; the MFMA path publishes one key
+  // per tile, and only when sampling.
+  const bool mfma = M > kGemvMaxRows;
   p.off_tile_keys = off;
-  off += align_up((size_t)M * p.tiles * k * 8, 256);
+  off += align_up((size_t)M * p.tiles * (mfma ? 1 : k) * 8, 256);
   p.off_tile_ms = off;
   off += align_up((size_t)M * p.tiles * 8, 256);
   p.off_tile_z = off;  // sampling mode: z of each tile's drawn row
   off += align_up((size_t)M * p.tiles * 8, 256);
   p.off_hpack = off;  // MFMA path: h in B-operand order, 16 * NT rows x d
-  off += M > kGemvMaxRows ? align_up((size_t)((M + 15) / 16) * 16 * (size_t)VT_D_MAX * 2, 256) : 0;
+  off += mfma ? align_up((size_t)((M + 15) / 16) * 16 * (size_t)VT_D_MAX * 2, 256) : 0;
+  p.off_zbuf = off;  // MFMA path, top-k mode: logits [M][tiles * kTileRows] fp32
+  off += mfma ? align_up((size_t)M * p.tiles * kTileRows * 4, 256) : 0;
   p.bytes = off;
   return p;
 }
@@ -802,6 +957,8 @@ hipError_t launch_head_call(const uint16_t *h, int32_t M, int32_t d, const uint1
   a.off_lo = (uint32_t)offset;
   a.off_hi = (uint32_t)(offset >> 32);
   a.tile_z = reinterpret_cast<uint64_t *>(base + p.off_tile_z);
+  a.zbuf = reinterpret_cast<float *>(base + p.off_zbuf);
+  a.zpitch = p.tiles * kTileRows;
   // Up to kGemvMaxRows rows: one GEMV pass with the merge in the same
   // kernel. More rows: the MFMA skinny GEMM, then one merge workgroup per row.
   if (M <= kGemvMaxRows) return launch_gemv(a, stream);

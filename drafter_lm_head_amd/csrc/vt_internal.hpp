@@ -40,7 +40,7 @@ hipError_t launch_gather(const uint16_t *W, int32_t V, int32_t d,
 constexpr int kTileRows = 64;
 struct HeadPlan {
   int32_t tiles;
-  size_t off_group, zero_bytes, off_tile_keys, off_tile_ms, off_tile_z, off_hpack;
+  size_t off_group, zero_bytes, off_tile_keys, off_tile_ms, off_tile_z, off_hpack, off_zbuf;
   size_t bytes;
 };
 HeadPlan head_plan(int32_t M, int32_t V_high, int32_t k);

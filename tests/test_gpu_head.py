@@ -68,8 +68,10 @@ def test_draft_tree_rows(dlh, M):
     check_case(dlh, h, W, t2f, 10)
 
 
-@pytest.mark.parametrize("V_high,d,k", [(1, 256, 1), (70, 520, 10), (129, 8, 64), (3000, 3584, 64)])
+@pytest.mark.parametrize("V_high,d,k", [(1, 256, 1), (70, 520, 10), (129, 8, 64), (3000, 3584, 64),
+                                         (4097, 64, 10), (8193, 128, 64), (12288, 64, 33)])
 def test_draft_tree_edges(dlh, V_high, d, k):
+    # Parts of 4096 logits per row: a part of one logit, several ragged ones.
     h, W, t2f = rand_case(300 + V_high, 60, d, V_high, hscale=2.0)
     check_case(dlh, h, W, t2f, min(k, V_high))
 
@@ -92,19 +94,31 @@ def test_k_range(dlh, k):
     check_case(dlh, h, W, t2f, k)
 
 
-def test_exact_ties_break_to_lower_full_id(dlh):
+@pytest.mark.parametrize("M,V_high", [(2, 700), (2, 5000), (6, 700), (6, 5000)])
+def test_exact_ties_break_to_lower_full_id(dlh, M, V_high):
     # All rows equal: every logit ties, so the picks are the k smallest full ids.
+    # With M > 4 and V_high = 5000 one part of a row holds 4096 tied logits,
+    # more than the survivor buffer: the exact max-round fallback runs.
     rng = np.random.default_rng(5)
-    d, V_high, k = 64, 700, 12
+    d, k = 64, 12
     row = synth.bf16_bits_from_f32(rng.standard_normal(d, dtype=np.float32))
     W = np.tile(row, (V_high, 1))
-    h = synth.bf16_bits_from_f32(rng.standard_normal((2, d), dtype=np.float32))
+    h = synth.bf16_bits_from_f32(rng.standard_normal((M, d), dtype=np.float32))
     t2f = rng.permutation(100_000)[:V_high].astype(np.int32)
     ids_g, probs_g = run_head(dlh, h, W, t2f, k)
     want = np.sort(t2f)[:k]
-    for m in range(2):
+    for m in range(M):
         np.testing.assert_array_equal(ids_g[m], want)
         np.testing.assert_allclose(probs_g[m], 1.0 / V_high, rtol=1e-5)
+
+
+@pytest.mark.parametrize("k", [10, 64])
+def test_draft_tree_max_vocab(dlh, k):
+    # The largest kept vocabulary with a full tree: 64 parts per row, and with
+    # k = 64 the merge ranks 64 x 64 part keys.
+    from drafter_lm_head_amd import VT_VHIGH_MAX
+    h, W, t2f = rand_case(11 + k, 64, 64, VT_VHIGH_MAX, hscale=3.0)
+    check_case(dlh, h, W, t2f, k)
 
 
 def test_hand_worked_example(dlh):
@@ -122,8 +136,9 @@ def test_hand_worked_example(dlh):
     np.testing.assert_allclose(probs_g, np.array(g["probs"]), rtol=2e-6)
 
 
-def test_determinism_and_counter_reset(dlh):
-    h, W, t2f = rand_case(7, 3, 1024, 20000)
+@pytest.mark.parametrize("M", [3, 20])
+def test_determinism_and_counter_reset(dlh, M):
+    h, W, t2f = rand_case(7, M, 1024, 20000)
     hd, Wd, td = to_dev_bf16(h), to_dev_bf16(W), to_dev_i32(t2f)
     M, d = h.shape
     n = dlh.vt_draft_head_workspace_size(M, 20000, d, 10)
