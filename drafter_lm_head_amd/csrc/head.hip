@@ -516,9 +516,14 @@ __global__ __launch_bounds__(WAVES *kWave) void head_gemv_kernel(HeadArgs a) {
 // k-chunk 4 s + l / 16 of k-step s, the same chunk for A and B, and receives
 // C[4 (l / 16) + r][l % 16] in accumulator register r. A workgroup owns a
 // tile of 64 W rows; its 4 waves split d into contiguous k ranges, stream
-// their slices of W once (16 KiB per wave in flight) and read h from L2. The partial products are summed over the waves in a fixed order
-// in LDS; each draft row's tile partial is then published exactly as on the
-// GEMV path, and a second kernel merges one draft row per workgroup.
+// their slices of W once (16 KiB per wave in flight) and read h from L2. The
+// partial products are summed over the waves in a fixed order in LDS. For
+// top-k the tile's logits go to the workspace and each draft row's softmax
+// partial over the tile is published; tree_merge_kernel then finds each
+// row's picks among the few tiles whose maximum can reach them. Ranking
+// inside every tile instead (as the GEMV path does for one to four rows)
+// costs hundreds of VALU instructions per (draft row, tile) pair, all of it
+// issued after the streaming ends. Sampling publishes each tile's draw.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
