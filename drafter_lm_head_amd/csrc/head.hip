@@ -55,21 +55,16 @@ __device__ __forceinline__ uint64_t pack_ms(float mu, float S) {
 __device__ __forceinline__ float ms_max(uint64_t v) { return __uint_as_float((uint32_t)v); }
 __device__ __forceinline__ float ms_sum(uint64_t v) { return __uint_as_float((uint32_t)(v >> 32)); }
 
-// The sampling key of tile row j of draft row m: (z + G) in key order, then
-// the lower full id; the draw is the largest key over all rows.
-__device__ __forceinline__ uint64_t sample_key(const HeadArgs &a, int m, int j, float z,
-                                               int32_t fid) {
-  return make_key(z + gumbel(a.seed_lo, a.seed_hi, a.off_lo, a.off_hi, m, j), fid);
-}
-
-// Sampling-mode tile partial of one draft row, by one wave (lane = tile row):
-// the tile's largest sampling key and that row's z, and the tile's softmax
-// partial over the unperturbed z.
+// Sampling-mode tile partial of one draft row, by one wave (lane = tile row,
+// g = its Gumbel variate): the tile's largest sampling key, (z + g) in key
+// order and then the lower full id, with that row's z, and the tile's
+// softmax partial over the unperturbed z. The draw is the largest key over
+// all tiles.
 __device__ __forceinline__ void wave_publish_sample(const HeadArgs &a, int m, int tile,
-                                                    int row0, float z, int32_t fid,
+                                                    float z, float g, int32_t fid,
                                                     bool valid) {
   const int lane = __lane_id();
-  const uint64_t key = valid ? sample_key(a, m, row0 + lane, z, fid) : 0ull;
+  const uint64_t key = valid ? make_key(z + g, fid) : 0ull;
   const uint64_t best = wave_max_u64(key);
   const uint64_t hit = __ballot(valid && key == best);
   const float zb = __shfl(z, hit ? (int)__builtin_ctzll(hit) : 0);
@@ -468,7 +463,10 @@ __global__ __launch_bounds__(WAVES *kWave) void head_gemv_kernel(HeadArgs a) {
 
   const bool valid = row0 + lane < a.V_high;
   if (a.sample) {  // one draw per draft row
-    if (wave < MT) wave_publish_sample(a, wave, tile, row0, s_z[wave][lane], fid, valid);
+    if (wave < MT)
+      wave_publish_sample(a, wave, tile, s_z[wave][lane],
+                          gumbel(a.seed_lo, a.seed_hi, a.off_lo, a.off_hi, wave, row0 + lane),
+                          fid, valid);
     if (arrive(a.counter, &s_slot) != (uint32_t)(a.tiles - 1)) return;
     for (int m = 0; m < MT; ++m) sample_merge<WAVES>(a, m, sh);
     if (threadIdx.x == 0) reset_counter(a.counter);
@@ -549,6 +547,12 @@ __global__ __launch_bounds__(kWave) void h_pack_kernel(const u32x4 *__restrict__
       (row < M && ch < c16) ? h[(size_t)row * c16 + ch] : u32x4{0, 0, 0, 0};
 }
 
+// With one or two 16-row column blocks the B operands are read straight
+// from h (16 rows x 64 bytes per load) and the packing kernel is skipped;
+// with more blocks the scattered reads cost more than the extra kernel.
+template <int NT>
+constexpr bool kDirectH = NT <= 2;
+
 template <int NT>
 __global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a) {
   union alignas(16) Smem {
@@ -598,9 +602,18 @@ __global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a
 #pragma unroll
     for (int t = 0; t < kStageChunks / 4; ++t) {
       const bool ok = base + 4 * t + g < c_hi;
-      const u32x4 *hs = a.hp + (size_t)((base / 4 + t) * NT) * kWave + lane;
+      if (kDirectH<NT>) {
+        const int ch = base + 4 * t + g;
 #pragma unroll
-      for (int cb = 0; cb < NT; ++cb) bv[t][cb] = ok ? hs[cb * kWave] : u32x4{0, 0, 0, 0};
+        for (int cb = 0; cb < NT; ++cb) {
+          const int row = cb * 16 + r16;
+          bv[t][cb] = (ok && row < M) ? a.h[(size_t)row * c16 + ch] : u32x4{0, 0, 0, 0};
+        }
+      } else {
+        const u32x4 *hs = a.hp + (size_t)((base / 4 + t) * NT) * kWave + lane;
+#pragma unroll
+        for (int cb = 0; cb < NT; ++cb) bv[t][cb] = ok ? hs[cb * kWave] : u32x4{0, 0, 0, 0};
+      }
     }
 #pragma unroll
     for (int t = 0; t < kStageChunks / 4; ++t) {
@@ -683,8 +696,18 @@ __global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a
 
   const bool valid = row0 + lane < a.V_high;
   const int32_t fid = valid ? a.t2f[row0 + lane] : 0;
-  for (int m = wave; m < M; m += kMfmaWaves)
-    wave_publish_sample(a, m, tile, row0, sm.part[0][m][lane], fid, valid);
+  // Draft rows in blocks of four: one Philox call per lane and block gives
+  // the variates of all four rows.
+  for (int b = wave; 4 * b < M; b += kMfmaWaves) {
+    const u32x4 x = gumbel_words(a.seed_lo, a.seed_hi, a.off_lo, a.off_hi, b, row0 + lane);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * b + r;
+      if (m < M)
+        wave_publish_sample(a, m, tile, sm.part[0][m][lane], gumbel_from_word(x[r]), fid,
+                            valid);
+    }
+  }
 }
 
 // Top-k merge of the MFMA path, one workgroup per draft row m, from the
@@ -851,10 +874,12 @@ __global__ __launch_bounds__(WAVES *kWave) void head_merge_kernel(HeadArgs a) {
 template <int NT>
 hipError_t launch_mfma(const HeadArgs &a, hipStream_t stream) {
   const int steps = (a.c16 + 3) / 4;
-  hipLaunchKernelGGL(h_pack_kernel, dim3(steps * NT), dim3(kWave), 0, stream, a.h, a.M,
-                     a.c16, NT, const_cast<u32x4 *>(a.hp));
-  hipError_t e0 = hipGetLastError();
-  if (e0 != hipSuccess) return e0;
+  if (!kDirectH<NT>) {
+    hipLaunchKernelGGL(h_pack_kernel, dim3(steps * NT), dim3(kWave), 0, stream, a.h, a.M,
+                       a.c16, NT, const_cast<u32x4 *>(a.hp));
+    hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
+  }
   hipLaunchKernelGGL((head_mfma_kernel<NT>), dim3(a.tiles), dim3(kMfmaWaves * kWave), 0,
                      stream, a);
   hipError_t e = hipGetLastError();
@@ -905,6 +930,8 @@ hipError_t launch_gemv(const HeadArgs &a, hipStream_t stream) {
 
 }  // namespace
 
+static_assert(kDirectH<2> && !kDirectH<3>, "packed h is allocated for more than 32 rows");
+
 HeadPlan head_plan(int32_t M, int32_t V_high, int32_t k) {
   // Fixed-offset prefix that every call leaves at zero: the ticket counter,
   // then the group maxima of up to VT_M_MAX draft rows. Per-call data after.
@@ -923,8 +950,8 @@ HeadPlan head_plan(int32_t M, int32_t V_high, int32_t k) {
   off += align_up((size_t)M * p.tiles * 8, 256);
   p.off_tile_z = off;  // sampling mode: z of each tile's drawn row
   off += align_up((size_t)M * p.tiles * 8, 256);
-  p.off_hpack = off;  // MFMA path: h in B-operand order, 16 * NT rows x d
-  off += mfma ? align_up((size_t)((M + 15) / 16) * 16 * (size_t)VT_D_MAX * 2, 256) : 0;
+  p.off_hpack = off;  // MFMA path past 32 rows: h in B-operand order, 16 * NT rows x d
+  off += M > 32 ? align_up((size_t)((M + 15) / 16) * 16 * (size_t)VT_D_MAX * 2, 256) : 0;
   p.off_zbuf = off;  // MFMA path, top-k mode: logits [M][tiles * kTileRows] fp32
   off += mfma ? align_up((size_t)M * p.tiles * kTileRows * 4, 256) : 0;
   p.bytes = off;

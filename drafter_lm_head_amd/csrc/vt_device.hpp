@@ -142,9 +142,9 @@ __device__ __forceinline__ int32_t key_id(uint64_t key) {
 // "Parallel random numbers: as easy as 1, 2, 3", SC 2011). Ten rounds of two
 // 32 x 32 -> 64-bit products of words 0 and 2 with fixed odd multipliers,
 // half swaps and key mixing; the key advances by two Weyl increments between
-// rounds. Only the first output word is used here.
-__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t c2,
-                                                 uint32_t c3, uint32_t k0, uint32_t k1) {
+// rounds.
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                               uint32_t c3, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
@@ -157,18 +157,28 @@ __device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint3
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
-  return c0;
+  return u32x4{c0, c1, c2, c3};
 }
 
-// Standard Gumbel variate of draft row m and trimmed index j for the draw
-// keyed by (seed, offset): counter (j, m, offset), key seed; the top 24 bits
-// x of the first word give u = (x + 1/2) / 2^24 in (0, 1) (exact in fp32),
-// and the variate is -log(-log u).
-__device__ __forceinline__ float gumbel(uint32_t seed_lo, uint32_t seed_hi, uint32_t off_lo,
-                                        uint32_t off_hi, int m, int j) {
-  const uint32_t x = philox_word0((uint32_t)j, (uint32_t)m, off_lo, off_hi, seed_lo, seed_hi);
+// Standard Gumbel variates of the draw keyed by (seed, offset): one Philox
+// call with counter (j, m / 4, offset) and key seed serves trimmed index j of
+// the four draft rows 4 (m / 4) .. 4 (m / 4) + 3, row m taking word m % 4.
+// The top 24 bits x of the word give u = (x + 1/2) / 2^24 in (0, 1) (exact
+// in fp32), and the variate is -log(-log u).
+__device__ __forceinline__ u32x4 gumbel_words(uint32_t seed_lo, uint32_t seed_hi,
+                                              uint32_t off_lo, uint32_t off_hi, int mblock,
+                                              int j) {
+  return philox4x32_10((uint32_t)j, (uint32_t)mblock, off_lo, off_hi, seed_lo, seed_hi);
+}
+__device__ __forceinline__ float gumbel_from_word(uint32_t x) {
   const float u = ((float)(x >> 8) + 0.5f) * 0x1p-24f;
   return -logf(-logf(u));
+}
+__device__ __forceinline__ float gumbel(uint32_t seed_lo, uint32_t seed_hi, uint32_t off_lo,
+                                        uint32_t off_hi, int m, int j) {
+  const u32x4 x = gumbel_words(seed_lo, seed_hi, off_lo, off_hi, m >> 2, j);
+  const int w = m & 3;
+  return gumbel_from_word(w == 0 ? x[0] : w == 1 ? x[1] : w == 2 ? x[2] : x[3]);
 }
 
 // -------------------------------------------------- cross-workgroup order

@@ -199,8 +199,9 @@ int vt_draft_head(const uint16_t *h, int32_t M, int32_t d,
  * probability exp(z_j) / sum_i exp(z_i):
  *   j*[m]       = argmax_j ( z[m, j] + G[m, j] )   (equal values: lower full id)
  *   G[m, j]     = -log(-log u),  u = (x + 1/2) / 2^24, x = the top 24 bits of
- *                 word 0 of Philox4x32-10 (Salmon et al., SC 2011) with
- *                 counter (j, m, offset low, offset high), key (seed low, high)
+ *                 word (m mod 4) of Philox4x32-10 (Salmon et al., SC 2011)
+ *                 with counter (j, m div 4, offset low, offset high) and key
+ *                 (seed low, seed high): one generator call serves four rows
  *   full_ids[m] = t2f[j*[m]],   probs[m] = exp(z[m, j*] - mu) / S  (as above)
  * z, mu and S are as for vt_draft_head (fp32 sums); G is computed in fp32.
  * The draw is a function of (seed, offset, m, logits) only: repeated calls

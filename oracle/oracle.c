@@ -340,18 +340,19 @@ void or_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2],
 }
 
 /* The Gumbel variate of draft row m and trimmed index j for a draw keyed by
- * (seed, offset): Philox4x32-10 with counter (j, m, offset low, offset high)
- * and key (seed low, seed high); the top 24 bits x of its first word give
- * the uniform u = (x + 1/2) / 2^24 in (0, 1), exactly representable; the
- * variate is -log(-log u). */
+ * (seed, offset): Philox4x32-10 with counter (j, m div 4, offset low, offset
+ * high) and key (seed low, seed high) yields four words, one for each of the
+ * draft rows 4 (m div 4) .. 4 (m div 4) + 3; row m takes word m mod 4. The
+ * top 24 bits x of that word give the uniform u = (x + 1/2) / 2^24 in (0, 1),
+ * exactly representable; the variate is -log(-log u). */
 double or_gumbel(uint64_t seed, uint64_t offset, int32_t m, int32_t j)
 {
-    const uint32_t ctr[4] = {(uint32_t)j, (uint32_t)m, (uint32_t)offset,
+    const uint32_t ctr[4] = {(uint32_t)j, (uint32_t)(m / 4), (uint32_t)offset,
                              (uint32_t)(offset >> 32)};
     const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
     uint32_t o[4];
     or_philox4x32_10(ctr, key, o);
-    const double u = ((double)(o[0] >> 8) + 0.5) / 16777216.0;
+    const double u = ((double)(o[m % 4] >> 8) + 0.5) / 16777216.0;
     return -log(-log(u));
 }
 

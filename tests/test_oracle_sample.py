@@ -111,3 +111,19 @@ def test_peaked_logits_draw_the_argmax():
     ids, probs, ti = oracle.draft_sample(h, W, t2f, seed=1, offset=0)
     assert (ti == 17).all() and (ids == 117).all()
     assert np.allclose(probs, 1.0)
+
+
+def test_rows_sharing_a_generator_call_are_independent():
+    # Rows 4b .. 4b + 3 take the four words of one Philox call: their
+    # variates must be uncorrelated (a row reading another row's word would
+    # give correlation 1), and rows of different blocks too.
+    n = 40000
+    g = oracle.gumbel(seed=77, offset=3, M=8, n=n)
+    bound = 5.0 / math.sqrt(n)
+    for r1, r2 in [(0, 1), (0, 2), (0, 3), (1, 2), (2, 3), (3, 4), (4, 7)]:
+        assert abs(stats.spearmanr(g[r1], g[r2]).statistic) < bound, (r1, r2)
+    # row m of block b is word m % 4 of the call with counter (j, b, offset)
+    j = 12345
+    x = oracle.philox4x32_10([j, 1, 3, 0], [77, 0])
+    u = ((x >> 8).astype(np.float64) + 0.5) / 2 ** 24
+    np.testing.assert_allclose(g[4:8, j], -np.log(-np.log(u)), rtol=0, atol=0)
