@@ -7,7 +7,10 @@ stream. The functions keep the C names:
 * ``vt_count_freq(ids, V)``            -> (counts uint32[V], n_invalid)
 * ``vt_select_vocab(counts, V_high)``  -> (t2f, f2t, sel_sum, tot_sum)
 * ``vt_gather_head(W, t2f)``           -> W_trim
+* ``vt_gather_bias(b, t2f)``           -> b_trim (heads with a bias)
 * ``vt_draft_head(h, W_trim, t2f, k)`` -> (full_ids int32[M, k], probs f32[M, k])
+* ``vt_draft_head_bias(h, W_trim, bias, t2f, k)``, ``vt_draft_sample(...)``,
+  ``vt_draft_sample_bias(...)``: the same with a bias, or one draw per row
 * ``vt_head_logits(h, W_trim)``        -> logits f32[M, V_high] (checks only)
 
 bfloat16 arrays may be passed as ``torch.bfloat16`` or as their 16-bit
@@ -27,6 +30,7 @@ __all__ = [
     "VtError", "lib", "lib_path", "VT_K_MAX", "VT_M_MAX", "VT_D_MAX",
     "VT_VHIGH_MAX", "vt_count_freq", "vt_select_vocab", "vt_gather_head",
     "vt_draft_head", "vt_draft_sample", "vt_head_logits", "vt_count_freq_workspace_size",
+    "vt_gather_bias", "vt_draft_head_bias", "vt_draft_sample_bias",
     "vt_select_vocab_workspace_size", "vt_draft_head_workspace_size",
     "coverage", "vt_coverage_curve", "vt_coverage_curve_workspace_size",
 ]
@@ -52,6 +56,10 @@ _SIGS = {
     "vt_draft_head_workspace_size": (_SZ, [_I32, _I32, _I32, _I32]),
     "vt_draft_head": (_INT, [_P, _I32, _I32, _P, _I32, _P, _I32, _P, _P, _P, _SZ, _P]),
     "vt_draft_sample": (_INT, [_P, _I32, _I32, _P, _I32, _P, _U64, _U64, _P, _P, _P, _SZ, _P]),
+    "vt_gather_bias": (_INT, [_P, _I32, _P, _I32, _P, _P, _P]),
+    "vt_draft_head_bias": (_INT, [_P, _I32, _I32, _P, _P, _I32, _P, _I32, _P, _P, _P, _SZ, _P]),
+    "vt_draft_sample_bias": (_INT, [_P, _I32, _I32, _P, _P, _I32, _P, _U64, _U64, _P, _P, _P, _SZ,
+                                    _P]),
     "vt_head_logits": (_INT, [_P, _I32, _I32, _P, _I32, _P, _P]),
     "vt_coverage_curve_workspace_size": (_SZ, [_I32, _I32]),
     "vt_coverage_curve": (_INT, [_P, _I32, _P, _I32, C.c_double, _P, _P, _P, _P, _SZ, _P]),
@@ -207,10 +215,25 @@ def vt_gather_head(W: torch.Tensor, t2f: torch.Tensor, out: torch.Tensor | None 
     return out
 
 
-def vt_draft_head(h: torch.Tensor, W_trim: torch.Tensor, t2f: torch.Tensor, k: int,
-                  full_ids: torch.Tensor | None = None, probs: torch.Tensor | None = None,
-                  ws: torch.Tensor | None = None):
-    """One draft step (VocabTrim Step 4): (full_ids[M, k], probs[M, k])."""
+def vt_gather_bias(b: torch.Tensor, t2f: torch.Tensor, out: torch.Tensor | None = None,
+                   n_bad: torch.Tensor | None = None) -> torch.Tensor:
+    """b_trim = b[t2f], the bias of a trimmed head (VocabTrim Step 3)."""
+    _dev(b, "b", _BF16, 1)
+    _dev(t2f, "t2f", (torch.int32,), 1)
+    V, V_high = b.numel(), t2f.numel()
+    if out is None:
+        out = torch.empty(V_high, dtype=b.dtype, device=b.device)
+    _dev(out, "out", _BF16, 1)
+    if out.numel() != V_high:
+        raise ValueError("out must hold V_high entries")
+    if n_bad is not None:
+        _dev(n_bad, "n_bad", (torch.int32, torch.uint32), 1)
+    _check(lib().vt_gather_bias(_ptr(b), V, _ptr(t2f), V_high, _ptr(out), _ptr(n_bad),
+                                _stream(b)), "vt_gather_bias")
+    return out
+
+
+def _head_shapes(h, W_trim, t2f, bias):
     _dev(h, "h", _BF16, 2)
     _dev(W_trim, "W_trim", _BF16, 2)
     _dev(t2f, "t2f", (torch.int32,), 1)
@@ -218,6 +241,29 @@ def vt_draft_head(h: torch.Tensor, W_trim: torch.Tensor, t2f: torch.Tensor, k: i
     V_high = W_trim.shape[0]
     if W_trim.shape[1] != d or t2f.numel() != V_high:
         raise ValueError("shape mismatch between h, W_trim and t2f")
+    if bias is not None:
+        _dev(bias, "bias", _BF16, 1)
+        if bias.numel() != V_high:
+            raise ValueError("bias must hold V_high entries")
+    return M, d, V_high
+
+
+def vt_draft_head(h: torch.Tensor, W_trim: torch.Tensor, t2f: torch.Tensor, k: int,
+                  full_ids: torch.Tensor | None = None, probs: torch.Tensor | None = None,
+                  ws: torch.Tensor | None = None):
+    """One draft step (VocabTrim Step 4): (full_ids[M, k], probs[M, k])."""
+    return _draft_head(h, W_trim, None, t2f, k, full_ids, probs, ws)
+
+
+def vt_draft_head_bias(h: torch.Tensor, W_trim: torch.Tensor, bias: torch.Tensor,
+                       t2f: torch.Tensor, k: int, full_ids: torch.Tensor | None = None,
+                       probs: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """vt_draft_head for a trimmed head with a bias bf16[V_high]."""
+    return _draft_head(h, W_trim, bias, t2f, k, full_ids, probs, ws)
+
+
+def _draft_head(h, W_trim, bias, t2f, k, full_ids, probs, ws):
+    M, d, V_high = _head_shapes(h, W_trim, t2f, bias)
     dev = h.device
     if full_ids is None:
         full_ids = torch.empty((M, k), dtype=torch.int32, device=dev)
@@ -230,9 +276,14 @@ def vt_draft_head(h: torch.Tensor, W_trim: torch.Tensor, t2f: torch.Tensor, k: i
     if ws is None:
         need = vt_draft_head_workspace_size(M, V_high, d, k)
         ws = _workspace(dev, "head", need, True)
-    _check(lib().vt_draft_head(_ptr(h), M, d, _ptr(W_trim), V_high, _ptr(t2f), k,
-                               _ptr(full_ids), _ptr(probs), _ptr(ws), ws.numel(), _stream(h)),
-           "vt_draft_head")
+    if bias is None:
+        _check(lib().vt_draft_head(_ptr(h), M, d, _ptr(W_trim), V_high, _ptr(t2f), k,
+                                   _ptr(full_ids), _ptr(probs), _ptr(ws), ws.numel(),
+                                   _stream(h)), "vt_draft_head")
+    else:
+        _check(lib().vt_draft_head_bias(_ptr(h), M, d, _ptr(W_trim), _ptr(bias), V_high,
+                                        _ptr(t2f), k, _ptr(full_ids), _ptr(probs), _ptr(ws),
+                                        ws.numel(), _stream(h)), "vt_draft_head_bias")
     return full_ids, probs
 
 
@@ -241,13 +292,19 @@ def vt_draft_sample(h: torch.Tensor, W_trim: torch.Tensor, t2f: torch.Tensor, se
                     probs: torch.Tensor | None = None, ws: torch.Tensor | None = None):
     """One sampled draft token per row (VocabTrim Step 4's multinomial draw,
     remapped): (full_ids[M], probs[M])."""
-    _dev(h, "h", _BF16, 2)
-    _dev(W_trim, "W_trim", _BF16, 2)
-    _dev(t2f, "t2f", (torch.int32,), 1)
-    M, d = h.shape
-    V_high = W_trim.shape[0]
-    if W_trim.shape[1] != d or t2f.numel() != V_high:
-        raise ValueError("shape mismatch between h, W_trim and t2f")
+    return _draft_sample(h, W_trim, None, t2f, seed, offset, full_ids, probs, ws)
+
+
+def vt_draft_sample_bias(h: torch.Tensor, W_trim: torch.Tensor, bias: torch.Tensor,
+                         t2f: torch.Tensor, seed: int, offset: int,
+                         full_ids: torch.Tensor | None = None,
+                         probs: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """vt_draft_sample for a trimmed head with a bias bf16[V_high]."""
+    return _draft_sample(h, W_trim, bias, t2f, seed, offset, full_ids, probs, ws)
+
+
+def _draft_sample(h, W_trim, bias, t2f, seed, offset, full_ids, probs, ws):
+    M, d, V_high = _head_shapes(h, W_trim, t2f, bias)
     dev = h.device
     if full_ids is None:
         full_ids = torch.empty(M, dtype=torch.int32, device=dev)
@@ -260,10 +317,16 @@ def vt_draft_sample(h: torch.Tensor, W_trim: torch.Tensor, t2f: torch.Tensor, se
     if ws is None:
         need = vt_draft_head_workspace_size(M, V_high, d, 1)
         ws = _workspace(dev, "head", need, True)
-    _check(lib().vt_draft_sample(_ptr(h), M, d, _ptr(W_trim), V_high, _ptr(t2f),
-                                 int(seed) & (2 ** 64 - 1), int(offset) & (2 ** 64 - 1),
-                                 _ptr(full_ids), _ptr(probs), _ptr(ws), ws.numel(), _stream(h)),
-           "vt_draft_sample")
+    seed, offset = int(seed) & (2 ** 64 - 1), int(offset) & (2 ** 64 - 1)
+    if bias is None:
+        _check(lib().vt_draft_sample(_ptr(h), M, d, _ptr(W_trim), V_high, _ptr(t2f), seed,
+                                     offset, _ptr(full_ids), _ptr(probs), _ptr(ws), ws.numel(),
+                                     _stream(h)), "vt_draft_sample")
+    else:
+        _check(lib().vt_draft_sample_bias(_ptr(h), M, d, _ptr(W_trim), _ptr(bias), V_high,
+                                          _ptr(t2f), seed, offset, _ptr(full_ids), _ptr(probs),
+                                          _ptr(ws), ws.numel(), _stream(h)),
+               "vt_draft_sample_bias")
     return full_ids, probs
 
 

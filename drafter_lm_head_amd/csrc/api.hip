@@ -114,6 +114,15 @@ int vt_gather_head(const uint16_t *W, int32_t V, int32_t d,
                                       as_stream(stream)));
 }
 
+int vt_gather_bias(const uint16_t *b, int32_t V, const int32_t *t2f, int32_t V_high,
+                   uint16_t *b_trim, uint32_t *n_bad, void *stream) {
+  if (!b || !t2f || !b_trim) return VT_ERR_INVALID_ARG;
+  if (V <= 0 || V_high <= 0) return VT_ERR_INVALID_ARG;
+  if (overlaps(b, (size_t)V * 2, b_trim, (size_t)V_high * 2)) return VT_ERR_INVALID_ARG;
+  return hip_status(vt::launch_gather_bias(b, V, t2f, V_high, b_trim, n_bad,
+                                           as_stream(stream)));
+}
+
 // ------------------------------------------------------------- draft head
 static int check_head(const uint16_t *h, int32_t M, int32_t d,
                       const uint16_t *W_trim, int32_t V_high) {
@@ -145,9 +154,24 @@ int vt_draft_head(const uint16_t *h, int32_t M, int32_t d,
   if (!ws || !aligned(ws, 256) ||
       ws_bytes < vt_draft_head_workspace_size(M, V_high, d, k))
     return VT_ERR_WORKSPACE;
-  return hip_status(vt::launch_draft_head(h, M, d, W_trim, V_high, t2f, k,
-                                          full_ids, probs, ws,
-                                          as_stream(stream)));
+  return hip_status(vt::launch_draft_head(h, M, d, W_trim, nullptr, V_high, t2f, k,
+                                          full_ids, probs, ws, as_stream(stream)));
+}
+
+int vt_draft_head_bias(const uint16_t *h, int32_t M, int32_t d,
+                       const uint16_t *W_trim, const uint16_t *bias, int32_t V_high,
+                       const int32_t *t2f, int32_t k, int32_t *full_ids, float *probs,
+                       void *ws, size_t ws_bytes, void *stream) {
+  int st = check_head(h, M, d, W_trim, V_high);
+  if (st != VT_OK) return st;
+  if (!bias || !t2f || !full_ids || !probs) return VT_ERR_INVALID_ARG;
+  if (k <= 0 || k > V_high) return VT_ERR_INVALID_ARG;
+  if (k > VT_K_MAX) return VT_ERR_UNSUPPORTED;
+  if (!ws || !aligned(ws, 256) ||
+      ws_bytes < vt_draft_head_workspace_size(M, V_high, d, k))
+    return VT_ERR_WORKSPACE;
+  return hip_status(vt::launch_draft_head(h, M, d, W_trim, bias, V_high, t2f, k, full_ids,
+                                          probs, ws, as_stream(stream)));
 }
 
 int vt_draft_sample(const uint16_t *h, int32_t M, int32_t d,
@@ -160,9 +184,23 @@ int vt_draft_sample(const uint16_t *h, int32_t M, int32_t d,
   if (!ws || !aligned(ws, 256) ||
       ws_bytes < vt_draft_head_workspace_size(M, V_high, d, 1))
     return VT_ERR_WORKSPACE;
-  return hip_status(vt::launch_draft_sample(h, M, d, W_trim, V_high, t2f, seed,
-                                            offset, full_ids, probs, ws,
-                                            as_stream(stream)));
+  return hip_status(vt::launch_draft_sample(h, M, d, W_trim, nullptr, V_high, t2f, seed,
+                                            offset, full_ids, probs, ws, as_stream(stream)));
+}
+
+int vt_draft_sample_bias(const uint16_t *h, int32_t M, int32_t d,
+                         const uint16_t *W_trim, const uint16_t *bias, int32_t V_high,
+                         const int32_t *t2f, uint64_t seed, uint64_t offset,
+                         int32_t *full_ids, float *probs, void *ws, size_t ws_bytes,
+                         void *stream) {
+  int st = check_head(h, M, d, W_trim, V_high);
+  if (st != VT_OK) return st;
+  if (!bias || !t2f || !full_ids) return VT_ERR_INVALID_ARG;
+  if (!ws || !aligned(ws, 256) ||
+      ws_bytes < vt_draft_head_workspace_size(M, V_high, d, 1))
+    return VT_ERR_WORKSPACE;
+  return hip_status(vt::launch_draft_sample(h, M, d, W_trim, bias, V_high, t2f, seed, offset,
+                                            full_ids, probs, ws, as_stream(stream)));
 }
 
 int vt_head_logits(const uint16_t *h, int32_t M, int32_t d,

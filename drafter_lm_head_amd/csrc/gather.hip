@@ -5,6 +5,8 @@
 // W_trim[i, :] = W[t2f[i], :]. A workgroup copies kGatherRows rows with
 // 16-byte loads and stores; each thread keeps kUnroll loads in flight before
 // storing. Reads and writes are streaming: neither array is reused here.
+// A head with a bias keeps the bias entries of the kept ids the same way
+// (the page's reconstruction copies them alongside the rows).
 #include "vt_internal.hpp"
 
 namespace vt {
@@ -55,7 +57,34 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(
   }
 }
 
+// Bias of the trimmed head: b_trim[i] = b[t2f[i]], zero for an entry
+// outside [0, V) (counted like a bad row).
+__global__ __launch_bounds__(kGatherThreads) void gather_bias_kernel(
+    const uint16_t *__restrict__ b, int32_t V, const int32_t *__restrict__ t2f,
+    int32_t V_high, uint16_t *__restrict__ out, uint32_t *__restrict__ n_bad) {
+  const int32_t i = blockIdx.x * kGatherThreads + threadIdx.x;
+  if (i >= V_high) return;
+  const int32_t src = t2f[i];
+  const bool ok = src >= 0 && src < V;
+  if (!ok && n_bad) atomicAdd(n_bad, 1u);
+  out[i] = ok ? b[src] : (uint16_t)0;
+}
+
 }  // namespace
+
+hipError_t launch_gather_bias(const uint16_t *b, int32_t V, const int32_t *t2f,
+                              int32_t V_high, uint16_t *b_trim, uint32_t *n_bad,
+                              hipStream_t stream) {
+  if (n_bad) {
+    hipLaunchKernelGGL(gather_clear_kernel, dim3(1), dim3(1), 0, stream, n_bad);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int32_t blocks = (V_high + kGatherThreads - 1) / kGatherThreads;
+  hipLaunchKernelGGL(gather_bias_kernel, dim3(blocks), dim3(kGatherThreads), 0, stream, b, V,
+                     t2f, V_high, b_trim, n_bad);
+  return hipGetLastError();
+}
 
 hipError_t launch_gather(const uint16_t *W, int32_t V, int32_t d,
                          const int32_t *t2f, int32_t V_high, uint16_t *W_trim,

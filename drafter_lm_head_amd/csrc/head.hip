@@ -45,6 +45,7 @@ struct HeadArgs {
   int32_t sample;
   uint32_t seed_lo, seed_hi, off_lo, off_hi;
   uint64_t *tile_z;      // [M][tiles]: bits of z of each tile's drawn row
+  const uint16_t *bias;  // bf16[V_high] added to every logit, or nullptr
   float *zbuf;           // MFMA path, top-k mode: logits [M][zpitch]
   int32_t zpitch;        // tiles * kTileRows floats
 };
@@ -462,9 +463,16 @@ __global__ __launch_bounds__(WAVES *kWave) void head_gemv_kernel(HeadArgs a) {
   __syncthreads();
 
   const bool valid = row0 + lane < a.V_high;
+  // Wave m < MT works on draft row m: its logit of tile row `lane`, with the
+  // head's bias when it has one.
+  float zl = 0.f;
+  if (wave < MT) {
+    zl = s_z[wave][lane];
+    if (a.bias && valid) zl += bf16_to_f32(a.bias[row0 + lane]);
+  }
   if (a.sample) {  // one draw per draft row
     if (wave < MT)
-      wave_publish_sample(a, wave, tile, s_z[wave][lane],
+      wave_publish_sample(a, wave, tile, zl,
                           gumbel(a.seed_lo, a.seed_hi, a.off_lo, a.off_hi, wave, row0 + lane),
                           fid, valid);
     if (arrive(a.counter, &s_slot) != (uint32_t)(a.tiles - 1)) return;
@@ -478,7 +486,7 @@ __global__ __launch_bounds__(WAVES *kWave) void head_gemv_kernel(HeadArgs a) {
   uint64_t *s_key = sh.cand;               // [MT][64] keys of the tile
   uint64_t *s_top = sh.cand + MT * kWave;  // [MT][64] ranked keys
   if (wave < MT) {
-    s_key[wave * kWave + lane] = valid ? make_key(s_z[wave][lane], fid) : 0ull;
+    s_key[wave * kWave + lane] = valid ? make_key(zl, fid) : 0ull;
     s_top[wave * kWave + lane] = 0;
   }
   __syncthreads();
@@ -489,7 +497,7 @@ __global__ __launch_bounds__(WAVES *kWave) void head_gemv_kernel(HeadArgs a) {
     __builtin_amdgcn_wave_barrier();
     const uint64_t key = s_top[m * kWave + lane];
     const float mu = key_logit(s_top[m * kWave]);
-    const float S = wave_sum(valid ? __expf(s_z[m][lane] - mu) : 0.f);
+    const float S = wave_sum(valid ? __expf(zl - mu) : 0.f);
     if (lane < k) publish_u64(a.tile_keys + ((size_t)m * a.tiles + tile) * k + lane, key);
     if (lane == 0) {
       publish_u64(a.tile_ms + (size_t)m * a.tiles + tile, pack_ms(mu, S));
@@ -650,6 +658,11 @@ __global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a
 #pragma unroll
     for (int w = 1; w < kMfmaWaves; ++w)
       val += *reinterpret_cast<const f32x4 *>(&sm.part[w][row][c4]);
+    if (a.bias) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (row0 + c4 + c < a.V_high) val[c] += bf16_to_f32(a.bias[row0 + c4 + c]);
+    }
     *reinterpret_cast<f32x4 *>(&sm.part[0][row][c4]) = val;
     if (!a.sample && row < M)
       *reinterpret_cast<f32x4 *>(a.zbuf + (size_t)row * a.zpitch + row0 + c4) = val;
@@ -960,13 +973,15 @@ HeadPlan head_plan(int32_t M, int32_t V_high, int32_t k) {
 
 namespace {
 hipError_t launch_head_call(const uint16_t *h, int32_t M, int32_t d, const uint16_t *W_trim,
-                            int32_t V_high, const int32_t *t2f, int32_t k, int32_t *full_ids,
+                            const uint16_t *bias, int32_t V_high, const int32_t *t2f,
+                            int32_t k, int32_t *full_ids,
                             float *probs, void *ws, bool sample, uint64_t seed,
                             uint64_t offset, hipStream_t stream) {
   const HeadPlan p = head_plan(M, V_high, k);
   char *base = static_cast<char *>(ws);
   HeadArgs a{};
   a.W = reinterpret_cast<const u32x4 *>(W_trim);
+  a.bias = bias;
   a.t2f = t2f;
   a.c16 = d / 8;
   a.V_high = V_high;
@@ -1004,19 +1019,19 @@ hipError_t launch_head_call(const uint16_t *h, int32_t M, int32_t d, const uint1
 }  // namespace
 
 hipError_t launch_draft_head(const uint16_t *h, int32_t M, int32_t d,
-                             const uint16_t *W_trim, int32_t V_high,
+                             const uint16_t *W_trim, const uint16_t *bias, int32_t V_high,
                              const int32_t *t2f, int32_t k, int32_t *full_ids,
                              float *probs, void *ws, hipStream_t stream) {
-  return launch_head_call(h, M, d, W_trim, V_high, t2f, k, full_ids, probs, ws, false, 0, 0,
-                          stream);
+  return launch_head_call(h, M, d, W_trim, bias, V_high, t2f, k, full_ids, probs, ws, false, 0,
+                          0, stream);
 }
 
 hipError_t launch_draft_sample(const uint16_t *h, int32_t M, int32_t d,
-                               const uint16_t *W_trim, int32_t V_high, const int32_t *t2f,
-                               uint64_t seed, uint64_t offset, int32_t *full_ids,
-                               float *probs, void *ws, hipStream_t stream) {
-  return launch_head_call(h, M, d, W_trim, V_high, t2f, 1, full_ids, probs, ws, true, seed,
-                          offset, stream);
+                               const uint16_t *W_trim, const uint16_t *bias, int32_t V_high,
+                               const int32_t *t2f, uint64_t seed, uint64_t offset,
+                               int32_t *full_ids, float *probs, void *ws, hipStream_t stream) {
+  return launch_head_call(h, M, d, W_trim, bias, V_high, t2f, 1, full_ids, probs, ws, true,
+                          seed, offset, stream);
 }
 
 hipError_t launch_head_logits(const uint16_t *h, int32_t M, int32_t d,

@@ -26,6 +26,11 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          false);
 }
 
+// bf16 payload -> fp32 (exact).
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
 __device__ __forceinline__ float dot8_bf16(u32x4 a, u32x4 b, float c) {
   c = dot2_bf16(a.x, b.x, c);
   c = dot2_bf16(a.y, b.y, c);

@@ -44,14 +44,18 @@ struct HeadPlan {
   size_t bytes;
 };
 HeadPlan head_plan(int32_t M, int32_t V_high, int32_t k);
+// bias: bf16[V_high] added to the logits, or nullptr for a head without one.
 hipError_t launch_draft_head(const uint16_t *h, int32_t M, int32_t d,
-                             const uint16_t *W_trim, int32_t V_high,
+                             const uint16_t *W_trim, const uint16_t *bias, int32_t V_high,
                              const int32_t *t2f, int32_t k, int32_t *full_ids,
                              float *probs, void *ws, hipStream_t stream);
 hipError_t launch_draft_sample(const uint16_t *h, int32_t M, int32_t d,
-                               const uint16_t *W_trim, int32_t V_high, const int32_t *t2f,
-                               uint64_t seed, uint64_t offset, int32_t *full_ids,
-                               float *probs, void *ws, hipStream_t stream);
+                               const uint16_t *W_trim, const uint16_t *bias, int32_t V_high,
+                               const int32_t *t2f, uint64_t seed, uint64_t offset,
+                               int32_t *full_ids, float *probs, void *ws, hipStream_t stream);
+hipError_t launch_gather_bias(const uint16_t *b, int32_t V, const int32_t *t2f,
+                              int32_t V_high, uint16_t *b_trim, uint32_t *n_bad,
+                              hipStream_t stream);
 // Coverage curve of a ranking.
 size_t coverage_ws_bytes(int32_t V, int32_t L);
 hipError_t launch_coverage(const uint32_t *counts, int32_t V, const int32_t *order, int32_t L,

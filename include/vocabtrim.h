@@ -156,6 +156,18 @@ int vt_gather_head(const uint16_t *W, int32_t V, int32_t d,
                    const int32_t *t2f, int32_t V_high, uint16_t *W_trim,
                    uint32_t *n_bad, void *stream);
 
+/* Bias of a trimmed head that has one: [VT] Step 3 copies the bias entries
+ * of the kept ids next to their rows when the original head carries a bias.
+ *
+ *   b_trim[i] = b[t2f[i]]   for i < V_high  (bit copy)
+ *
+ * b       device, bf16[V];  t2f as for vt_gather_head
+ * b_trim  device, bf16[V_high]; must not overlap b
+ * n_bad   as for vt_gather_head: entries outside [0, V) give 0 and are
+ *         counted when n_bad is not NULL. */
+int vt_gather_bias(const uint16_t *b, int32_t V, const int32_t *t2f, int32_t V_high,
+                   uint16_t *b_trim, uint32_t *n_bad, void *stream);
+
 /* ------------------------------------------------------------- draft head
  * One draft step of the trimmed head: [VT] Step 4 (logits of the trimmed
  * head, softmax over the trimmed vocabulary, pick, remap trimmed -> full id
@@ -191,6 +203,16 @@ int vt_draft_head(const uint16_t *h, int32_t M, int32_t d,
                   int32_t k, int32_t *full_ids, float *probs, void *ws,
                   size_t ws_bytes, void *stream);
 
+/* vt_draft_head for a trimmed head with a bias ([VT] Step 3 keeps the bias
+ * of the kept ids; the trimmed head is a linear layer with that bias):
+ *   z[m, j] = sum_t h[m, t] * W_trim[j, t] + bias[j]   (fp32)
+ * and everything else as for vt_draft_head.
+ * bias  device, bf16[V_high] (e.g. from vt_gather_bias); not NULL. */
+int vt_draft_head_bias(const uint16_t *h, int32_t M, int32_t d,
+                       const uint16_t *W_trim, const uint16_t *bias, int32_t V_high,
+                       const int32_t *t2f, int32_t k, int32_t *full_ids, float *probs,
+                       void *ws, size_t ws_bytes, void *stream);
+
 /* ------------------------------------------------------------ draft sample
  * One draft token per row drawn from the subset softmax: the multinomial
  * draw of [VT] Step 4's draft loop (softmax over the trimmed logits, one
@@ -216,6 +238,15 @@ int vt_draft_sample(const uint16_t *h, int32_t M, int32_t d,
                     const uint16_t *W_trim, int32_t V_high, const int32_t *t2f,
                     uint64_t seed, uint64_t offset, int32_t *full_ids,
                     float *probs, void *ws, size_t ws_bytes, void *stream);
+
+/* vt_draft_sample for a trimmed head with a bias: z as for
+ * vt_draft_head_bias, the draw as for vt_draft_sample.
+ * bias  device, bf16[V_high]; not NULL. */
+int vt_draft_sample_bias(const uint16_t *h, int32_t M, int32_t d,
+                         const uint16_t *W_trim, const uint16_t *bias, int32_t V_high,
+                         const int32_t *t2f, uint64_t seed, uint64_t offset,
+                         int32_t *full_ids, float *probs, void *ws, size_t ws_bytes,
+                         void *stream);
 
 /* ------------------------------------------------------- logits (checks)
  * The trimmed logits alone, z[m, j] as defined for vt_draft_head, written to

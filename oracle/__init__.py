@@ -51,8 +51,8 @@ def _load():
             lib.or_logits.argtypes = [P, i32, i32, P, i32, P]
             lib.or_softmax.argtypes = [P, i32, i32, P, P, P]
             lib.or_topk.argtypes = [P, P, i32, i32, i32, P, P]
-            lib.or_draft_head.argtypes = [P, i32, i32, P, i32, P, i32, P, P, P, P, P]
-            lib.or_draft_sample.argtypes = [P, i32, i32, P, i32, P, u64, u64, P, P, P, P]
+            lib.or_draft_head.argtypes = [P, i32, i32, P, P, i32, P, i32, P, P, P, P, P]
+            lib.or_draft_sample.argtypes = [P, i32, i32, P, P, i32, P, u64, u64, P, P, P, P]
             lib.or_philox4x32_10.argtypes = [P, P, P]
             lib.or_philox4x32_10.restype = None
             lib.or_gumbel.argtypes = [u64, u64, i32, i32]
@@ -172,8 +172,18 @@ def topk(z, t2f, k: int):
     return ids, ti
 
 
-def draft_head(h, W_trim, t2f, k: int, want_logits: bool = False):
-    """One draft-head call: logits, subset softmax, top-k, remap.
+def _bias(bias, V_high):
+    if bias is None:
+        return None
+    b = _arr(bias, np.uint16, 1)
+    if b.size != V_high:
+        raise ValueError("bias must have V_high entries")
+    return b
+
+
+def draft_head(h, W_trim, t2f, k: int, want_logits: bool = False, bias=None):
+    """One draft-head call: logits (plus the head's bf16 bias when given; VocabTrim
+    page, Step 3 keeps it), subset softmax, top-k, remap.
 
     Returns ``(full_ids int32[M, k], probs float32[M, k])`` and, with
     ``want_logits``, also ``(z fp64[M, V_high], mu[M], S[M])``.
@@ -185,12 +195,13 @@ def draft_head(h, W_trim, t2f, k: int, want_logits: bool = False):
     V_high = W_trim.shape[0]
     if W_trim.shape[1] != d or t2f.size != V_high:
         raise ValueError("shape mismatch")
+    b = _bias(bias, V_high)
     ids = np.empty((M, k), np.int32)
     probs = np.empty((M, k), np.float32)
     z = np.empty((M, V_high), np.float64) if want_logits else None
     mu = np.empty(M, np.float64)
     S = np.empty(M, np.float64)
-    _ok(_load().or_draft_head(_p(h), M, d, _p(W_trim), V_high, _p(t2f), k,
+    _ok(_load().or_draft_head(_p(h), M, d, _p(W_trim), _p(b), V_high, _p(t2f), k,
                               _p(ids), _p(probs), _p(z), _p(mu), _p(S)), "draft_head")
     if want_logits:
         return ids, probs, (z, mu, S)
@@ -213,7 +224,7 @@ def gumbel(seed: int, offset: int, M: int, n: int):
     return g
 
 
-def draft_sample(h, W_trim, t2f, seed: int, offset: int, want_logits: bool = False):
+def draft_sample(h, W_trim, t2f, seed: int, offset: int, want_logits: bool = False, bias=None):
     """One multinomial draw per row from the subset softmax (Gumbel-max with
     Philox uniforms), remapped through t2f (VocabTrim page, Step 4).
 
@@ -227,11 +238,12 @@ def draft_sample(h, W_trim, t2f, seed: int, offset: int, want_logits: bool = Fal
     V_high = W_trim.shape[0]
     if W_trim.shape[1] != d or t2f.size != V_high:
         raise ValueError("shape mismatch")
+    b = _bias(bias, V_high)
     ids = np.empty(M, np.int32)
     probs = np.empty(M, np.float32)
     ti = np.empty(M, np.int32)
     z = np.empty((M, V_high), np.float64) if want_logits else None
-    _ok(_load().or_draft_sample(_p(h), M, d, _p(W_trim), V_high, _p(t2f), C.c_uint64(seed),
+    _ok(_load().or_draft_sample(_p(h), M, d, _p(W_trim), _p(b), V_high, _p(t2f), C.c_uint64(seed),
                                 C.c_uint64(offset), _p(ids), _p(probs), _p(ti), _p(z)),
         "draft_sample")
     if want_logits:

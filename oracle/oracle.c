@@ -261,16 +261,27 @@ int or_topk(const double *z, const int32_t *t2f, int32_t M, int32_t V_high,
     return OR_OK;
 }
 
+/* The bias term of a head that carries one ([VT] Step 3 keeps the bias of
+ * the kept ids; the trimmed head is a linear layer with that bias):
+ *   z[m, j] += bias[j]   for m < M, j < rows (bias as bf16 payloads). */
+static void add_bias(double *z, int32_t M, int32_t rows, const uint16_t *bias)
+{
+    for (int32_t m = 0; m < M; ++m)
+        for (int32_t j = 0; j < rows; ++j)
+            z[(size_t)m * rows + j] += bf16_value(bias[j]);
+}
+
 /* One draft-head call, composed from the steps above:
- * logits over the trimmed head, softmax over the subset, top-k, remap.
+ * logits over the trimmed head (plus its bias when bias is not NULL),
+ * softmax over the subset, top-k, remap.
  *   full_ids[m, r] = t2f of the r-th largest logit of row m
  *   probs[m, r]    = its subset-softmax probability, rounded to float
  * z_out (may be NULL) receives the fp64 logits [M, V_high]; mu_out and
  * S_out (may be NULL) the per-row max and sum. */
 int or_draft_head(const uint16_t *h, int32_t M, int32_t d,
-                  const uint16_t *W_trim, int32_t V_high, const int32_t *t2f,
-                  int32_t k, int32_t *full_ids, float *probs, double *z_out,
-                  double *mu_out, double *S_out)
+                  const uint16_t *W_trim, const uint16_t *bias, int32_t V_high,
+                  const int32_t *t2f, int32_t k, int32_t *full_ids, float *probs,
+                  double *z_out, double *mu_out, double *S_out)
 {
     if (!h || !W_trim || !t2f || !full_ids || !probs || M <= 0 || d <= 0 ||
         V_high <= 0 || k <= 0 || k > V_high)
@@ -285,6 +296,8 @@ int or_draft_head(const uint16_t *h, int32_t M, int32_t d,
         goto done;
     if ((rc = or_logits(h, M, d, W_trim, V_high, z)) != OR_OK)
         goto done;
+    if (bias)
+        add_bias(z, M, V_high, bias);
     if ((rc = or_softmax(z, M, V_high, NULL, mu, S)) != OR_OK)
         goto done;
     if ((rc = or_topk(z, t2f, M, V_high, k, full_ids, ti)) != OR_OK)
@@ -370,15 +383,16 @@ int or_gumbel_block(uint64_t seed, uint64_t offset, int32_t M, int32_t n, double
 
 /* One sampled draft token per row, the page's multinomial draw from the
  * subset softmax ([VT] Step 4's draft loop), by the Gumbel-max rule: the
- * draw is argmax_j (z[m, j] + G[m, j]) with independent standard Gumbel
+ * draw is argmax_j (z[m, j] + G[m, j]) (z with the bias when bias is not
+ * NULL) with independent standard Gumbel
  * variates G, which picks j with probability exp(z_j) / sum_i exp(z_i).
  * Equal perturbed logits: the lower full id. Outputs:
  *   full_ids[m] = t2f[j*],  probs[m] = p[m, j*] (subset softmax, float)
  *   trim_idx[m] = j* (may be NULL); z_out [M, V_high] (may be NULL). */
 int or_draft_sample(const uint16_t *h, int32_t M, int32_t d,
-                    const uint16_t *W_trim, int32_t V_high, const int32_t *t2f,
-                    uint64_t seed, uint64_t offset, int32_t *full_ids,
-                    float *probs, int32_t *trim_idx, double *z_out)
+                    const uint16_t *W_trim, const uint16_t *bias, int32_t V_high,
+                    const int32_t *t2f, uint64_t seed, uint64_t offset,
+                    int32_t *full_ids, float *probs, int32_t *trim_idx, double *z_out)
 {
     if (!h || !W_trim || !t2f || !full_ids || !probs || M <= 0 || d <= 0 ||
         V_high <= 0)
@@ -392,6 +406,8 @@ int or_draft_sample(const uint16_t *h, int32_t M, int32_t d,
         goto done;
     if ((rc = or_logits(h, M, d, W_trim, V_high, z)) != OR_OK)
         goto done;
+    if (bias)
+        add_bias(z, M, V_high, bias);
     if ((rc = or_softmax(z, M, V_high, NULL, mu, S)) != OR_OK)
         goto done;
     for (int32_t m = 0; m < M; ++m) {

@@ -101,7 +101,7 @@ def logit_bound(h, W):
     return gamma * (hf @ Wf.T)
 
 
-def check_draws(ids_g, probs_g, h, W, t2f, seed, offset):
+def check_draws(ids_g, probs_g, h, W, t2f, seed, offset, bias=None):
     """Checks GPU draws (one per row) against the oracle's Gumbel-max draws
     on the same (seed, offset). A different pick is accepted only where the
     two candidates' perturbed logits z + G are within the fp32 error of the
@@ -111,7 +111,8 @@ def check_draws(ids_g, probs_g, h, W, t2f, seed, offset):
     import oracle
     ids_g = np.asarray(ids_g).ravel()
     probs_g = np.asarray(probs_g, dtype=np.float64).ravel()
-    ids_o, probs_o, ti_o, z = oracle.draft_sample(h, W, t2f, seed, offset, want_logits=True)
+    ids_o, probs_o, ti_o, z = oracle.draft_sample(h, W, t2f, seed, offset, want_logits=True,
+                                                  bias=bias)
     M, n = z.shape
     G = oracle.gumbel(seed, offset, M, n)
     v = z + G

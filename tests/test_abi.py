@@ -193,3 +193,27 @@ def test_coverage_curve_validation(lib):
     assert f(A, 100, A, 10, 0.9, A, None, None, A, n, None) == INVALID
     assert f(A, 100000, A, 50000, 0.9, A, A, None, None, n, None) == WORKSPACE
     assert f(A, 100000, A, 50000, 0.9, A, A, None, A, n - 1, None) == WORKSPACE
+
+
+def test_bias_entry_points_validation(lib):
+    far = A + (1 << 40)
+    g = lib.vt_gather_bias
+    assert g(None, 100, A, 10, far, None, None) == INVALID
+    assert g(A, 100, None, 10, far, None, None) == INVALID
+    assert g(A, 100, A, 10, None, None, None) == INVALID
+    assert g(A, 0, A, 10, far, None, None) == INVALID
+    assert g(A, 100, A, 0, far, None, None) == INVALID
+    assert g(A, 100, A, 10, A + 100, None, None) == INVALID              # overlap
+    n = lib.vt_draft_head_workspace_size(3, 32768, 4096, 10)
+    hb = lib.vt_draft_head_bias
+    assert hb(A, 3, 4096, A, None, 32768, A, 10, A, A, A, n, None) == INVALID   # no bias
+    assert hb(A, 3, 4096, A, A, 32768, A, 0, A, A, A, n, None) == INVALID
+    assert hb(A, 65, 4096, A, A, 32768, A, 10, A, A, A, n, None) == UNSUPPORTED
+    assert hb(A, 3, 4096, A, A, 32768, A, 10, A, A, A, n - 1, None) == WORKSPACE
+    assert hb(A + 2, 3, 4096, A, A, 32768, A, 10, A, A, A, n, None) == INVALID
+    n1 = lib.vt_draft_head_workspace_size(3, 32768, 4096, 1)
+    sb = lib.vt_draft_sample_bias
+    assert sb(A, 3, 4096, A, None, 32768, A, 1, 2, A, A, A, n1, None) == INVALID
+    assert sb(A, 3, 4096, A, A, 32768, None, 1, 2, A, A, A, n1, None) == INVALID
+    assert sb(A, 3, 4096, A, A, 32768, A, 1, 2, A, A, None, n1, None) == WORKSPACE
+    assert sb(A, 3, 4096, A, A, 32768, A, 1, 2, A, A, A, n1 - 1, None) == WORKSPACE

@@ -226,3 +226,53 @@ def test_head_shrink_figure():
     assert 1 - g["trimmed_vocab_k"] / g["full_vocab_k"] == g["compute_cut"]
     w = synth.WORKLOADS["llama3_8b"]
     assert abs((1 - w.V_high / w.V) - g["compute_cut"]) < 0.01
+
+
+# ------------------------------------------------------------------ bias
+# A head that carries a bias keeps the bias of the kept ids (VocabTrim page,
+# Step 3); the trimmed head is then a linear layer with that bias.
+def test_bias_gather_is_a_copy_of_the_kept_entries():
+    rng = np.random.default_rng(40)
+    b = rng.integers(0, 2**16, size=500, dtype=np.uint16)
+    t2f = rng.permutation(500)[:123].astype(np.int32)
+    out = oracle.gather(b[:, None], t2f)[:, 0]
+    assert out.tobytes() == b[t2f].tobytes()
+
+
+def test_zero_weights_pick_the_largest_bias():
+    # With W = 0 every logit is its bias: the picks are the k largest bias
+    # values (equal values: lower full id) and the probabilities their softmax.
+    rng = np.random.default_rng(41)
+    V_high, d, k = 300, 16, 12
+    bias_f = np.round(rng.standard_normal(V_high) * 4) / 4   # many exact ties
+    bias = bf(bias_f.astype(np.float32))
+    bv = f32(bias).astype(np.float64)
+    W = np.zeros((V_high, d), np.uint16)
+    h = rand_bf16(rng, (3, d))
+    t2f = rng.permutation(10_000)[:V_high].astype(np.int32)
+    ids, probs, (z, mu, S) = oracle.draft_head(h, W, t2f, k, want_logits=True, bias=bias)
+    order = sorted(range(V_high), key=lambda j: (-bv[j], t2f[j]))[:k]
+    p = np.exp(bv - logsumexp(bv))
+    for m in range(3):
+        np.testing.assert_array_equal(z[m], bv)
+        assert ids[m].tolist() == [int(t2f[j]) for j in order]
+        np.testing.assert_allclose(probs[m], p[order], rtol=1e-6)
+
+
+def test_bias_shifts_every_logit_by_its_entry():
+    rng = np.random.default_rng(42)
+    V_high, d = 200, 64
+    W = rand_bf16(rng, (V_high, d), 0.1)
+    h = rand_bf16(rng, (2, d))
+    bias = rand_bf16(rng, V_high, 2.0)
+    t2f = np.arange(V_high, dtype=np.int32)
+    _, _, (z0, _, _) = oracle.draft_head(h, W, t2f, 5, want_logits=True)
+    _, _, (z1, _, _) = oracle.draft_head(h, W, t2f, 5, want_logits=True, bias=bias)
+    np.testing.assert_allclose(z1 - z0, np.broadcast_to(f32(bias), z0.shape), rtol=0,
+                               atol=1e-12)
+    # a constant bias leaves the softmax unchanged
+    c = bf(np.full(V_high, 3.5, np.float32))
+    i0, p0 = oracle.draft_head(h, W, t2f, 7)
+    i1, p1 = oracle.draft_head(h, W, t2f, 7, bias=c)
+    np.testing.assert_array_equal(i0, i1)
+    np.testing.assert_allclose(p0, p1, rtol=1e-6)

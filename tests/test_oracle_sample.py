@@ -127,3 +127,20 @@ def test_rows_sharing_a_generator_call_are_independent():
     x = oracle.philox4x32_10([j, 1, 3, 0], [77, 0])
     u = ((x >> 8).astype(np.float64) + 0.5) / 2 ** 24
     np.testing.assert_allclose(g[4:8, j], -np.log(-np.log(u)), rtol=0, atol=0)
+
+
+def test_biased_draw_follows_the_bias_softmax():
+    # W = 0 and bias = z: the draw histogram is softmax(bias) (chi-square).
+    from scipy.special import softmax as sp_softmax
+    bvals = np.array([1.0, -0.5, 2.25, 0.0, -2.0, 0.75], np.float32)
+    bias = synth.bf16_bits_from_f32(bvals)
+    p = sp_softmax(synth.f32_from_bf16_bits(bias).astype(np.float64))
+    W = np.zeros((6, 8), np.uint16)
+    h = np.zeros((3000, 8), np.uint16)
+    t2f = np.array([5, 50, 500, 5000, 6, 60], np.int32)
+    counts = np.zeros(6)
+    for off in range(8):
+        ids, probs, ti = oracle.draft_sample(h, W, t2f, seed=11, offset=off, bias=bias)
+        np.testing.assert_allclose(probs, p[ti].astype(np.float32), rtol=1e-6)
+        counts += np.bincount(ti, minlength=6)
+    assert stats.chisquare(counts, counts.sum() * p).pvalue > 1e-4
