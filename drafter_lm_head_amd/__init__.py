@@ -39,7 +39,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libvocabtrim.so")
 
 VT_OK, VT_ERR_INVALID_ARG, VT_ERR_UNSUPPORTED, VT_ERR_WORKSPACE, VT_ERR_HIP = 0, -1, -2, -3, -4
-VT_K_MAX, VT_M_MAX, VT_D_MAX, VT_VHIGH_MAX = 64, 64, 8192, 262144
+VT_K_MAX, VT_M_MAX, VT_D_MAX, VT_VHIGH_MAX = 64, 512, 8192, 262144
 
 _lock = threading.Lock()
 _lib = None

@@ -46,6 +46,8 @@ struct HeadArgs {
   uint32_t seed_lo, seed_hi, off_lo, off_hi;
   uint64_t *tile_z;      // [M][tiles]: bits of z of each tile's drawn row
   const uint16_t *bias;  // bf16[V_high] added to every logit, or nullptr
+  int32_t cgroups;       // MFMA path: groups of kGroupRows draft rows
+  int32_t ntt;           // MFMA path: 16-row column blocks over all M rows
   float *zbuf;           // MFMA path, top-k mode: logits [M][zpitch]
   int32_t zpitch;        // tiles * kTileRows floats
 };
@@ -534,6 +536,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMfmaWaves = 4;
+constexpr int kGroupRows = 64;  // draft rows per MFMA workgroup (4 column blocks)
 
 // W is staged through wave-private LDS: the operand layout (16 rows x 64
 // bytes per load) is slow to fetch from HBM directly, so each load
@@ -569,8 +572,17 @@ __global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a
   };
   __shared__ Smem sm;
   const int lane = __lane_id(), wave = threadIdx.x / kWave;
-  const int tile = blockIdx.x, row0 = tile * kTileRows;
-  const int c16 = a.c16, M = a.M;
+  // Workgroup -> (tile, group of draft rows). Workgroup b runs on XCD b % 8;
+  // the groups of one tile take consecutive slots of the same XCD, so that
+  // the tile is read from HBM once and served to the other groups from that
+  // XCD's L2. One group (M <= 64) is the identity map.
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int cg = slot % a.cgroups, tile = xcd + 8 * (slot / a.cgroups);
+  if (tile >= a.tiles) return;
+  const int row0 = tile * kTileRows;
+  const int mb = cg * kGroupRows;               // first draft row of the group
+  const int M = min(kGroupRows, a.M - mb);      // draft rows of the group
+  const int c16 = a.c16;
   const int g = lane >> 4, r16 = lane & 15;
   // This wave's contiguous range of 16-byte chunks (a multiple of 4).
   const int cq = ((c16 + kMfmaWaves - 1) / kMfmaWaves + 3) / 4 * 4;
@@ -615,12 +627,15 @@ __global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a
 #pragma unroll
         for (int cb = 0; cb < NT; ++cb) {
           const int row = cb * 16 + r16;
-          bv[t][cb] = (ok && row < M) ? a.h[(size_t)row * c16 + ch] : u32x4{0, 0, 0, 0};
+          bv[t][cb] = (ok && row < M) ? a.h[(size_t)(mb + row) * c16 + ch] : u32x4{0, 0, 0, 0};
         }
       } else {
-        const u32x4 *hs = a.hp + (size_t)((base / 4 + t) * NT) * kWave + lane;
+        // Column blocks past the last draft row (a partial last group) are
+        // not packed: their operands are zero.
+        const u32x4 *hs = a.hp + (size_t)((base / 4 + t) * a.ntt + 4 * cg) * kWave + lane;
 #pragma unroll
-        for (int cb = 0; cb < NT; ++cb) bv[t][cb] = ok ? hs[cb * kWave] : u32x4{0, 0, 0, 0};
+        for (int cb = 0; cb < NT; ++cb)
+          bv[t][cb] = (ok && 4 * cg + cb < a.ntt) ? hs[cb * kWave] : u32x4{0, 0, 0, 0};
       }
     }
 #pragma unroll
@@ -665,7 +680,7 @@ __global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a
     }
     *reinterpret_cast<f32x4 *>(&sm.part[0][row][c4]) = val;
     if (!a.sample && row < M)
-      *reinterpret_cast<f32x4 *>(a.zbuf + (size_t)row * a.zpitch + row0 + c4) = val;
+      *reinterpret_cast<f32x4 *>(a.zbuf + (size_t)(mb + row) * a.zpitch + row0 + c4) = val;
   }
   __syncthreads();
   if (!a.sample) {
@@ -702,7 +717,7 @@ __global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a
         const float mw = qm[w * kWave + lane];
         if (mw != -INFINITY) S += qs[w * kWave + lane] * __expf(mw - mu);
       }
-      a.tile_ms[(size_t)m * a.tiles + tile] = pack_ms(mu, S);
+      a.tile_ms[(size_t)(mb + m) * a.tiles + tile] = pack_ms(mu, S);
     }
     return;
   }
@@ -712,13 +727,14 @@ __global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a
   // Draft rows in blocks of four: one Philox call per lane and block gives
   // the variates of all four rows.
   for (int b = wave; 4 * b < M; b += kMfmaWaves) {
-    const u32x4 x = gumbel_words(a.seed_lo, a.seed_hi, a.off_lo, a.off_hi, b, row0 + lane);
+    const u32x4 x =
+        gumbel_words(a.seed_lo, a.seed_hi, a.off_lo, a.off_hi, mb / 4 + b, row0 + lane);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = 4 * b + r;
       if (m < M)
-        wave_publish_sample(a, m, tile, sm.part[0][m][lane], gumbel_from_word(x[r]), fid,
-                            valid);
+        wave_publish_sample(a, mb + m, tile, sm.part[0][m][lane], gumbel_from_word(x[r]),
+                            fid, valid);
     }
   }
 }
@@ -888,12 +904,13 @@ template <int NT>
 hipError_t launch_mfma(const HeadArgs &a, hipStream_t stream) {
   const int steps = (a.c16 + 3) / 4;
   if (!kDirectH<NT>) {
-    hipLaunchKernelGGL(h_pack_kernel, dim3(steps * NT), dim3(kWave), 0, stream, a.h, a.M,
-                       a.c16, NT, const_cast<u32x4 *>(a.hp));
+    hipLaunchKernelGGL(h_pack_kernel, dim3(steps * a.ntt), dim3(kWave), 0, stream, a.h, a.M,
+                       a.c16, a.ntt, const_cast<u32x4 *>(a.hp));
     hipError_t e0 = hipGetLastError();
     if (e0 != hipSuccess) return e0;
   }
-  hipLaunchKernelGGL((head_mfma_kernel<NT>), dim3(a.tiles), dim3(kMfmaWaves * kWave), 0,
+  const int slots = (a.tiles + 7) / 8 * a.cgroups;  // per XCD
+  hipLaunchKernelGGL((head_mfma_kernel<NT>), dim3(8 * slots), dim3(kMfmaWaves * kWave), 0,
                      stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -947,12 +964,12 @@ static_assert(kDirectH<2> && !kDirectH<3>, "packed h is allocated for more than 
 
 HeadPlan head_plan(int32_t M, int32_t V_high, int32_t k) {
   // Fixed-offset prefix that every call leaves at zero: the ticket counter,
-  // then the group maxima of up to VT_M_MAX draft rows. Per-call data after.
+  // then the group maxima of the GEMV path's draft rows. Per-call data after.
   HeadPlan p;
   p.tiles = (V_high + kTileRows - 1) / kTileRows;
   size_t off = 256;
   p.off_group = off;
-  off += (size_t)VT_M_MAX * 2 * kGroups * 8;
+  off += (size_t)kGemvMaxRows * 2 * kGroups * 8;
   p.zero_bytes = off;
   // Tile keys: k per tile on the GEMV path; the MFMA path publishes one key
   // per tile, and only when sampling.
@@ -991,7 +1008,7 @@ hipError_t launch_head_call(const uint16_t *h, int32_t M, int32_t d, const uint1
   a.tile_keys = reinterpret_cast<uint64_t *>(base + p.off_tile_keys);
   a.tile_ms = reinterpret_cast<uint64_t *>(base + p.off_tile_ms);
   a.group_max = reinterpret_cast<uint64_t *>(base + p.off_group);
-  a.group_kth = a.group_max + (size_t)VT_M_MAX * kGroups;
+  a.group_kth = a.group_max + (size_t)kGemvMaxRows * kGroups;
   a.tiles_per_group = (p.tiles + kGroups - 1) / kGroups;
   a.hp = reinterpret_cast<const u32x4 *>(base + p.off_hpack);
   a.M = M;
@@ -1006,6 +1023,8 @@ hipError_t launch_head_call(const uint16_t *h, int32_t M, int32_t d, const uint1
   a.tile_z = reinterpret_cast<uint64_t *>(base + p.off_tile_z);
   a.zbuf = reinterpret_cast<float *>(base + p.off_zbuf);
   a.zpitch = p.tiles * kTileRows;
+  a.cgroups = (M + kGroupRows - 1) / kGroupRows;
+  a.ntt = (M + 15) / 16;
   // Up to kGemvMaxRows rows: one GEMV pass with the merge in the same
   // kernel. More rows: the MFMA skinny GEMM, then one merge workgroup per row.
   if (M <= kGemvMaxRows) return launch_gemv(a, stream);

@@ -46,7 +46,7 @@ extern "C" {
 
 /* Limits of this build. */
 #define VT_K_MAX 64           /* top-k per draft row                        */
-#define VT_M_MAX 64           /* draft rows per vt_draft_head call           */
+#define VT_M_MAX 512          /* draft rows per vt_draft_head call           */
 #define VT_D_MAX 8192         /* hidden size; d must also be a multiple of 8 */
 #define VT_VHIGH_MAX 262144   /* kept vocabulary per vt_draft_head call     */
 

@@ -108,7 +108,8 @@ def test_gather_validation(lib):
 def test_draft_head_validation(lib):
     n = lib.vt_draft_head_workspace_size(1, 32768, 4096, 10)
     assert n > 0
-    assert lib.vt_draft_head_workspace_size(65, 32768, 4096, 10) == 0
+    assert lib.vt_draft_head_workspace_size(513, 32768, 4096, 10) == 0
+    assert lib.vt_draft_head_workspace_size(512, 32768, 4096, 10) > 0
     assert lib.vt_draft_head_workspace_size(1, 32768, 4096, 65) == 0
     f = lib.vt_draft_head
     args = dict(h=A, M=1, d=4096, W=A, V_high=32768, t2f=A, k=10, ids=A, probs=A,
@@ -120,7 +121,7 @@ def test_draft_head_validation(lib):
                  a["probs"], a["ws"], a["ws_n"], None)
 
     assert call(M=0) == INVALID
-    assert call(M=65) == UNSUPPORTED
+    assert call(M=513) == UNSUPPORTED
     assert call(d=4100) == INVALID
     assert call(d=8200) == INVALID
     assert call(V_high=0) == INVALID
@@ -144,7 +145,7 @@ def test_head_logits_validation(lib):
     assert f(A, 1, 4096, A, 32768, None, None) == INVALID
     assert f(A, 0, 4096, A, 32768, A, None) == INVALID
     assert f(A, 1, 4095, A, 32768, A, None) == INVALID
-    assert f(A, 65, 4096, A, 32768, A, None) == UNSUPPORTED
+    assert f(A, 513, 4096, A, 32768, A, None) == UNSUPPORTED
 
 
 def test_binding_fails_loudly_without_gpu_tensors():
@@ -170,7 +171,7 @@ def test_draft_sample_validation(lib):
                  a["ids"], a["probs"], a["ws"], a["ws_n"], None)
 
     assert call(M=0) == INVALID
-    assert call(M=65) == UNSUPPORTED
+    assert call(M=513) == UNSUPPORTED
     assert call(d=4100) == INVALID
     assert call(V_high=0) == INVALID
     assert call(h=A + 2) == INVALID
@@ -208,7 +209,7 @@ def test_bias_entry_points_validation(lib):
     hb = lib.vt_draft_head_bias
     assert hb(A, 3, 4096, A, None, 32768, A, 10, A, A, A, n, None) == INVALID   # no bias
     assert hb(A, 3, 4096, A, A, 32768, A, 0, A, A, A, n, None) == INVALID
-    assert hb(A, 65, 4096, A, A, 32768, A, 10, A, A, A, n, None) == UNSUPPORTED
+    assert hb(A, 513, 4096, A, A, 32768, A, 10, A, A, A, n, None) == UNSUPPORTED
     assert hb(A, 3, 4096, A, A, 32768, A, 10, A, A, A, n - 1, None) == WORKSPACE
     assert hb(A + 2, 3, 4096, A, A, 32768, A, 10, A, A, A, n, None) == INVALID
     n1 = lib.vt_draft_head_workspace_size(3, 32768, 4096, 1)

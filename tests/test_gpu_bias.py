@@ -52,7 +52,7 @@ def test_gather_bias_copies_kept_entries_and_counts_bad_ones(dlh):
     assert oracle.gather(b[:, None], t2f[good])[:, 0].tobytes() == got[good].tobytes()
 
 
-@pytest.mark.parametrize("M", [1, 3, 4, 5, 20, 60])
+@pytest.mark.parametrize("M", [1, 3, 4, 5, 20, 60, 130])
 def test_biased_head_matches_oracle(dlh, M):
     # GEMV path up to 4 rows, the MFMA path beyond; V_high is ragged.
     h, W, b, t2f = biased_case(100 + M, M, 512, 3001)
@@ -100,7 +100,7 @@ def test_biased_head_full_size(dlh, M):
     check_picks(ids.cpu().numpy(), probs.cpu().numpy(), z_o, t2f, w.k, ids_o)
 
 
-@pytest.mark.parametrize("M", [2, 9])
+@pytest.mark.parametrize("M", [2, 9, 70])
 def test_biased_draws_match_oracle(dlh, M):
     h, W, b, t2f = biased_case(300 + M, M, 256, 2000, bias_std=2.0)
     near = 0

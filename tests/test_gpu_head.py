@@ -61,18 +61,22 @@ def test_draft_rows(dlh, M):
     check_case(dlh, h, W, t2f, 10)
 
 
-@pytest.mark.parametrize("M", [17, 33, 60, 64])
+@pytest.mark.parametrize("M", [17, 33, 60, 64, 65, 100, 128, 257, 512])
 def test_draft_tree_rows(dlh, M):
-    # M > 4 runs the MFMA skinny GEMM and one merge workgroup per row.
+    # M > 4 runs the MFMA skinny GEMM and one merge workgroup per row; past
+    # 64 rows the workgroups take groups of 64 draft rows of each tile.
     h, W, t2f = rand_case(200 + M, M, 1024, 2500)
     check_case(dlh, h, W, t2f, 10)
 
 
-@pytest.mark.parametrize("V_high,d,k", [(1, 256, 1), (70, 520, 10), (129, 8, 64), (3000, 3584, 64),
-                                         (4097, 64, 10), (8193, 128, 64), (12288, 64, 33)])
-def test_draft_tree_edges(dlh, V_high, d, k):
-    # Parts of 4096 logits per row: a part of one logit, several ragged ones.
-    h, W, t2f = rand_case(300 + V_high, 60, d, V_high, hscale=2.0)
+@pytest.mark.parametrize("V_high,d,k,M", [(1, 256, 1, 60), (70, 520, 10, 60), (129, 8, 64, 60),
+                                           (3000, 3584, 64, 60), (4097, 64, 10, 60),
+                                           (8193, 128, 64, 60), (12288, 64, 33, 60),
+                                           (4097, 520, 33, 130), (65, 8, 64, 193)])
+def test_draft_tree_edges(dlh, V_high, d, k, M):
+    # Ragged tiles and row groups: a last tile of one row, a last group of
+    # two (M = 130) or one (M = 193) draft rows.
+    h, W, t2f = rand_case(300 + V_high, M, d, V_high, hscale=2.0)
     check_case(dlh, h, W, t2f, min(k, V_high))
 
 
@@ -112,13 +116,29 @@ def test_exact_ties_break_to_lower_full_id(dlh, M, V_high):
         np.testing.assert_allclose(probs_g[m], 1.0 / V_high, rtol=1e-5)
 
 
-@pytest.mark.parametrize("k", [10, 64])
-def test_draft_tree_max_vocab(dlh, k):
-    # The largest kept vocabulary with a full tree: 64 parts per row, and with
-    # k = 64 the merge ranks 64 x 64 part keys.
+@pytest.mark.parametrize("k,M", [(10, 64), (64, 64), (10, 128)])
+def test_draft_tree_max_vocab(dlh, k, M):
+    # The largest kept vocabulary (4096 tiles per row) with full trees; with
+    # k = 64 many tiles reach the merge's bound.
     from drafter_lm_head_amd import VT_VHIGH_MAX
-    h, W, t2f = rand_case(11 + k, 64, 64, VT_VHIGH_MAX, hscale=3.0)
+    h, W, t2f = rand_case(11 + k + M, M, 64, VT_VHIGH_MAX, hscale=3.0)
     check_case(dlh, h, W, t2f, k)
+
+
+def test_widest_tree_full_size_sampled_rows(dlh):
+    # VT_M_MAX draft rows on the LLaMA-3-8B head shape (a seeded random head):
+    # rows are independent, so a sample of them is checked against the oracle
+    # run on those rows alone (the first and last of several row groups).
+    from drafter_lm_head_amd import VT_M_MAX
+    w = synth.WORKLOADS["llama3_8b"]
+    rng = np.random.default_rng(512)
+    Wt = synth.bf16_bits_from_f32(rng.standard_normal((w.V_high, w.d), dtype=np.float32) * np.float32(0.02))
+    t2f = rng.permutation(w.V)[: w.V_high].astype(np.int32)
+    h = synth.make_hidden(w, M=VT_M_MAX)
+    ids_g, probs_g = run_head(dlh, h, Wt, t2f, w.k)
+    rows = [0, 1, 63, 64, 200, 447, 448, VT_M_MAX - 1]
+    ids_o, _, (z_o, _, _) = oracle.draft_head(h[rows], Wt, t2f, w.k, want_logits=True)
+    check_picks(ids_g[rows], probs_g[rows], z_o, t2f, w.k, ids_o)
 
 
 def test_hand_worked_example(dlh):
@@ -136,7 +156,7 @@ def test_hand_worked_example(dlh):
     np.testing.assert_allclose(probs_g, np.array(g["probs"]), rtol=2e-6)
 
 
-@pytest.mark.parametrize("M", [3, 20])
+@pytest.mark.parametrize("M", [3, 20, 200])
 def test_determinism_and_counter_reset(dlh, M):
     h, W, t2f = rand_case(7, M, 1024, 20000)
     hd, Wd, td = to_dev_bf16(h), to_dev_bf16(W), to_dev_i32(t2f)
@@ -151,9 +171,9 @@ def test_determinism_and_counter_reset(dlh, M):
             ref = cur
         assert cur == ref
     torch.cuda.synchronize()
-    # the ticket counter and the group maxima (a fixed 256 + 64*2*64*8-byte
-    # prefix) are back at zero for the next call
-    assert int(ws[:256 + 64 * 2 * 64 * 8].to(torch.int64).sum().item()) == 0
+    # the ticket counter and the GEMV path's group maxima (a fixed
+    # 256 + 4*2*64*8-byte prefix) are back at zero for the next call
+    assert int(ws[:256 + 4 * 2 * 64 * 8].to(torch.int64).sum().item()) == 0
 
 
 def test_full_vocab_equals_untrimmed_head(dlh):

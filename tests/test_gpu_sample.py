@@ -48,12 +48,12 @@ def test_tiny_pipeline_draws_match_oracle(dlh):
     assert near <= 1
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 16, 33, 60, 64])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 16, 33, 60, 64, 65, 130, 512])
 def test_draws_match_oracle_gemv_and_mfma(dlh, M):
     h, W, t2f = rand_case(100 + M, M, 512, 3000, hscale=6.0)   # ragged V_high
     for off in (0, 1, 2**40 + 5):
         ids, probs = draw(dlh, h, W, t2f, 0xDEADBEEF12345, off)
-        assert check_draws(ids, probs, h, W, t2f, 0xDEADBEEF12345, off) <= 1
+        assert check_draws(ids, probs, h, W, t2f, 0xDEADBEEF12345, off) <= max(1, M // 64)
 
 
 def test_draws_are_reproducible_and_move_with_offset(dlh):
@@ -75,7 +75,7 @@ def _exact_head(z, rows):
     return h, W, synth.f32_from_bf16_bits(zb).astype(np.float64)
 
 
-@pytest.mark.parametrize("M", [4, 64])
+@pytest.mark.parametrize("M", [4, 64, 256])
 def test_gpu_draws_follow_the_softmax(dlh, M):
     # Draws from a 6-token subset with exactly known logits: the histogram
     # over many (row, offset) draws matches softmax(z) (chi-square).
