@@ -599,25 +599,23 @@ __global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a
 #pragma unroll
     for (int cb = 0; cb < NT; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 v[kStageChunks];
   // Stage loads: instruction q covers tile rows 4q .. 4q + 3, 256 bytes each.
-  auto load_stage = [&](int base) {
+  auto load_stage = [&](u32x4 (&v)[kStageChunks], int base) {
     const int ch = base + r16;
 #pragma unroll
     for (int q = 0; q < kStageChunks; ++q)
       v[q] = ch < c_hi ? load_stream16(tileW + min(4 * q + g, last_row) * c16 + ch)
                        : u32x4{0, 0, 0, 0};
   };
-  if (c_lo < c_hi) load_stage(c_lo);
-#pragma unroll 1
-  for (int base = c_lo; base < c_hi; base += kStageChunks) {
+  // One stage: its loads (v) go to LDS, v is refilled with the stage `ahead`
+  // chunks further on, then the B operands of the whole stage (contiguous
+  // loads from L2) and per k-step the A operands from LDS and the MFMAs; the
+  // scheduling barriers keep the compiler from hoisting every A read.
+  auto do_stage = [&](u32x4 (&v)[kStageChunks], int base, int ahead) {
 #pragma unroll
     for (int q = 0; q < kStageChunks; ++q) st[(4 * q + g) * kStagePitch + r16] = v[q];
     __builtin_amdgcn_wave_barrier();
-    if (base + kStageChunks < c_hi) load_stage(base + kStageChunks);
-    // B operands of the whole stage (contiguous loads from L2), then per
-    // k-step the A operands from LDS and the MFMAs; the barriers keep the
-    // compiler from hoisting every A read (register pressure).
+    if (base + ahead < c_hi) load_stage(v, base + ahead);
     u32x4 bv[kStageChunks / 4][NT];
 #pragma unroll
     for (int t = 0; t < kStageChunks / 4; ++t) {
@@ -630,8 +628,6 @@ __global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a
           bv[t][cb] = (ok && row < M) ? a.h[(size_t)(mb + row) * c16 + ch] : u32x4{0, 0, 0, 0};
         }
       } else {
-        // Column blocks past the last draft row (a partial last group) are
-        // not packed: their operands are zero.
         const u32x4 *hs = a.hp + (size_t)((base / 4 + t) * a.ntt + 4 * cg) * kWave + lane;
 #pragma unroll
         for (int cb = 0; cb < NT; ++cb)
@@ -641,7 +637,7 @@ __global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a
 #pragma unroll
     for (int t = 0; t < kStageChunks / 4; ++t) {
       __builtin_amdgcn_sched_barrier(0);
-      const int cl = 4 * t + g;  // chunk within the stage for this lane
+      const int cl = 4 * t + g;
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
         const u32x4 av = st[(rb * 16 + r16) * kStagePitch + cl];
@@ -653,7 +649,11 @@ __global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a
       }
     }
     __builtin_amdgcn_wave_barrier();
-  }
+  };
+  u32x4 v[kStageChunks];
+  if (c_lo < c_hi) load_stage(v, c_lo);
+#pragma unroll 1
+  for (int base = c_lo; base < c_hi; base += kStageChunks) do_stage(v, base, kStageChunks);
   __syncthreads();  // every wave is done with its stage before part[] reuses it
 
   // Partial products to LDS as [draft row][tile row] (rows padded to break
