@@ -388,7 +388,10 @@ constexpr int kGemvWaves = 8;
 
 template <int WAVES, int MT, int CPL, bool RAGGED, bool LOGITS>
 __global__ __launch_bounds__(WAVES *kWave) void head_gemv_kernel(HeadArgs a) {
-  constexpr int U = 1;  // rows per wave and step
+  // Rows per wave and step: short rows (small d) take several per step so
+  // that about 8 loads per lane are in flight; from 6 loads per row on, one
+  // row per step measured best.
+  constexpr int U = CPL >= 6 ? 1 : CPL >= 3 ? 2 : CPL == 2 ? 4 : 8;
   static_assert(kTileRows % (WAVES * U) == 0, "tile must split evenly");
   static_assert(MT <= WAVES, "one wave per draft row in the epilogue");
   __shared__ float s_z[MT][kTileRows];
