@@ -296,7 +296,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic() if (w.name == "llama3_8b" and M == 1) else None,
-                     "kernel": "head_gemv_kernel" if M <= 4 else
+                     "kernel": "head_gemv_kernel" if M <= 2 else
                                "h_pack_kernel + head_mfma_kernel + head_merge_kernel",
                      "bytes_per_launch": nb,
                      "us_per_launch": round(ms_step * 1000, 3),
@@ -319,7 +319,7 @@ def main():
                  "v_high_for_90pct": v_high_90},
         "pipeline_us": round(us_pipe, 2),
     }
-    if M > 4:
+    if M > 2:
         # The wide-tree path is a dense bf16 contraction on the matrix cores: report its
         # rate against the dense bf16 peak. M is padded to whole 16-row MFMA tiles.
         fl = 2.0 * M * V_high * d

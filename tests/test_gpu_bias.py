@@ -54,7 +54,7 @@ def test_gather_bias_copies_kept_entries_and_counts_bad_ones(dlh):
 
 @pytest.mark.parametrize("M", [1, 3, 4, 5, 20, 60, 130])
 def test_biased_head_matches_oracle(dlh, M):
-    # GEMV path up to 4 rows, the MFMA path beyond; V_high is ragged.
+    # GEMV path up to 2 rows, the MFMA path beyond; V_high is ragged.
     h, W, b, t2f = biased_case(100 + M, M, 512, 3001)
     k = 10
     ids, probs = dlh.vt_draft_head_bias(to_dev_bf16(h), to_dev_bf16(W), to_dev_bf16(b),
