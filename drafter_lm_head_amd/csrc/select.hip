@@ -17,6 +17,10 @@
 // Counts of a frequency histogram are very skewed (most ids share a few
 // small values), so digit histograms combine each wave's most common digit
 // into one LDS atomic; loads are 16 bytes wide with several in flight.
+// From kMtMinV ids on, the selection runs over many workgroups instead (see
+// below).
+#include <algorithm>
+
 #include "vt_internal.hpp"
 
 namespace vt {
@@ -341,21 +345,311 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   }
 }
 
+// ------------------------------------------------------- many workgroups
+// A large vocabulary is selected by the whole chip. Id v gets the key
+// (counts[v] << 32) | ~v: the keys are distinct and a larger key is exactly a
+// higher rank (count descending, id ascending), so the kept set is
+// {v : key(v) >= P} for P the V_high-th largest key, with no tie rule left to
+// apply at the cut:
+//   1. P by radix select over the 64 key bits, six digits (11 bits, the last
+//      9): each pass histograms the keys that share the digits chosen so far
+//      (per-workgroup LDS histograms folded into one with atomics) and the
+//      last workgroup to finish picks the next digit;
+//   2. the kept keys are compacted (in any order) and their counts summed;
+//   3. blocks of kSortBlock keys are sorted in LDS (bitonic, descending); the
+//      rank of a key is its position in its block plus the number of larger
+//      keys in every other block (binary search), summed over groups of
+//      blocks in a fixed order;
+//   4. t2f[rank] = id and f2t[id] = rank.
+constexpr int kSortBlock = 2048;  // keys per sorted block (two per thread)
+constexpr int kRankGroup = 4;     // blocks searched per rank workgroup (at least)
+constexpr int kRankGroupsMax = 32;  // partial ranks summed per key (at most)
+constexpr int kPasses = 6;
+
+struct MtState {
+  unsigned long long pref, mask, tot, sel;
+  uint32_t rank, ticket, ncomp, pad;
+};
+
+__device__ __forceinline__ uint64_t sel_key(uint32_t c, int32_t v) {
+  return ((uint64_t)c << 32) | (uint32_t)(~(uint32_t)v);
+}
+__device__ __forceinline__ uint32_t fetch_u32(const uint32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ __launch_bounds__(256) void mt_init_kernel(MtState *st, uint32_t *ghist,
+                                                      int32_t V_high, int32_t *f2t, int32_t V) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i == 0) {
+    st->pref = 0;
+    st->mask = 0;
+    st->tot = 0;
+    st->sel = 0;
+    st->rank = (uint32_t)V_high;
+    st->ticket = 0;
+    st->ncomp = 0;
+  }
+  if (i < 2048) ghist[i] = 0;
+  if (f2t && i < V) f2t[i] = -1;
+}
+
+// One radix-select pass over the ids of this workgroup (4 per thread).
+__global__ __launch_bounds__(kSelThreads) void mt_hist_kernel(const uint32_t *counts,
+                                                              int32_t V, MtState *st,
+                                                              uint32_t *ghist, int pass) {
+  __shared__ SelShared s;
+  __shared__ uint32_t s_slot;
+  const int tid = threadIdx.x;
+  const int lo = pass < kPasses - 1 ? 53 - 11 * pass : 0;
+  const uint32_t nbins = pass < kPasses - 1 ? 2048u : 512u;
+  for (int i = tid; i < 2048; i += kSelThreads) s.hist[i] = 0;
+  const uint64_t pref = st->pref, mask = st->mask;
+  __syncthreads();
+  const int32_t i4 = blockIdx.x * kSelThreads + tid;
+  const u32x4 q = 4 * i4 < V ? load_counts4(counts, V, i4) : u32x4{0, 0, 0, 0};
+  unsigned long long tsum = 0;
+  const uint32_t qc[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int32_t v = 4 * i4 + c;
+    const uint64_t key = sel_key(qc[c], v);
+    const bool active = v < V && ((key ^ pref) & mask) == 0;
+    hist_add(s.hist, (uint32_t)(key >> lo) & (nbins - 1), active);
+    if (v < V) tsum += qc[c];
+  }
+  __syncthreads();
+  for (uint32_t i = tid; i < nbins; i += kSelThreads)
+    if (s.hist[i])
+      __hip_atomic_fetch_add(&ghist[i], s.hist[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (pass == 0) {
+    tsum = block_sum_u64(tsum, s);
+    if (tid == 0 && tsum)
+      __hip_atomic_fetch_add(&st->tot, tsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (arrive(&st->ticket, &s_slot) != gridDim.x - 1) return;
+
+  // Last workgroup: the digit holding the rank-th largest key. Thread t
+  // takes digits nbins - 1 - 2t and nbins - 2 - 2t (descending order).
+  const int d0 = (int)nbins - 1 - 2 * tid, d1 = d0 - 1;
+  const uint32_t h0 = d0 >= 0 ? fetch_u32(&ghist[d0]) : 0u;
+  const uint32_t h1 = d1 >= 0 ? fetch_u32(&ghist[d1]) : 0u;
+  uint32_t total;
+  const uint32_t before = block_excl_scan(h0 + h1, s, &total);
+  const uint32_t r = st->rank;
+  const uint64_t dmask = (uint64_t)(nbins - 1) << lo;
+  if (d0 >= 0 && before < r && r <= before + h0) {
+    st->pref = pref | ((uint64_t)d0 << lo);
+    st->mask = mask | dmask;
+    st->rank = r - before;
+  } else if (d1 >= 0 && before + h0 < r && r <= before + h0 + h1) {
+    st->pref = pref | ((uint64_t)d1 << lo);
+    st->mask = mask | dmask;
+    st->rank = r - before - h0;
+  }
+  for (uint32_t i = tid; i < nbins; i += kSelThreads)
+    __hip_atomic_store(&ghist[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) reset_counter(&st->ticket);
+}
+
+// The kept keys (key >= P) to comp[], in any order, and the sum of their counts.
+__global__ __launch_bounds__(kSelThreads) void mt_compact_kernel(const uint32_t *counts,
+                                                                 int32_t V, MtState *st,
+                                                                 uint64_t *comp) {
+  __shared__ SelShared s;
+  __shared__ uint32_t s_base;
+  const int tid = threadIdx.x;
+  const uint64_t P = st->pref;
+  const int32_t i4 = blockIdx.x * kSelThreads + tid;
+  const u32x4 q = 4 * i4 < V ? load_counts4(counts, V, i4) : u32x4{0, 0, 0, 0};
+  const uint32_t qc[4] = {q.x, q.y, q.z, q.w};
+  bool keep[4];
+  uint32_t nk = 0;
+  unsigned long long csum = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int32_t v = 4 * i4 + c;
+    keep[c] = v < V && sel_key(qc[c], v) >= P;
+    nk += keep[c];
+    if (keep[c]) csum += qc[c];
+  }
+  uint32_t total;
+  const uint32_t excl = block_excl_scan(nk, s, &total);
+  csum = block_sum_u64(csum, s);
+  if (tid == 0) {
+    s_base = total ? __hip_atomic_fetch_add(&st->ncomp, total, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT)
+                   : 0u;
+    if (csum)
+      __hip_atomic_fetch_add(&st->sel, csum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  uint32_t o = s_base + excl;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    if (keep[c]) comp[o++] = sel_key(qc[c], 4 * i4 + c);
+}
+
+// Sorts block b of the n compacted keys descending in LDS (0 pads the block).
+__global__ __launch_bounds__(kSelThreads) void mt_block_sort_kernel(const uint64_t *comp,
+                                                                    int32_t n,
+                                                                    uint64_t *sorted) {
+  __shared__ uint64_t sk[kSortBlock];
+  const int tid = threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.x * kSortBlock;
+  for (int i = tid; i < kSortBlock; i += kSelThreads)
+    sk[i] = base + i < n ? comp[base + i] : 0ull;
+  __syncthreads();
+  for (uint32_t size = 2; size <= (uint32_t)kSortBlock; size <<= 1)
+    for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+      const uint32_t i = tid;  // kSortBlock / 2 compare-exchanges, one per thread
+      const uint32_t lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
+      const uint64_t x = sk[lo], y = sk[hi];
+      if ((x < y) == ((lo & size) == 0)) {
+        sk[lo] = y;
+        sk[hi] = x;
+      }
+      __syncthreads();
+    }
+  for (int i = tid; i < kSortBlock; i += kSelThreads) sorted[base + i] = sk[i];
+}
+
+// Number of keys in the descending block ob that are larger than x.
+__device__ __forceinline__ uint32_t count_greater(const uint64_t *ob, uint64_t x) {
+  uint32_t lo = 0, hi = kSortBlock;
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi) >> 1;
+    if (ob[mid] > x) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// Partial ranks of the keys of block b against the blocks of group g (blocks
+// g * group .. g * group + group - 1): rank_part[g][j] for position
+// j = b * kSortBlock + i.
+__global__ __launch_bounds__(kSelThreads) void mt_rank_kernel(const uint64_t *sorted, int32_t nb,
+                                                              int32_t ngroups, int32_t group,
+                                                              uint32_t *rank_part) {
+  __shared__ uint64_t ob[kSortBlock];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x / ngroups, g = blockIdx.x % ngroups;
+  const int64_t npos = (int64_t)nb * kSortBlock;
+  const int64_t j0 = (int64_t)b * kSortBlock + tid, j1 = j0 + kSelThreads;
+  const uint64_t x0 = sorted[j0], x1 = sorted[j1];
+  uint32_t r0 = 0, r1 = 0;
+  const int ob_end = min(nb, (g + 1) * group);
+  for (int o = g * group; o < ob_end; ++o) {
+    if (o == b) {  // within its own sorted block a key's rank is its position
+      r0 += tid;
+      r1 += tid + kSelThreads;
+      continue;
+    }
+    __syncthreads();
+    ob[tid] = sorted[(int64_t)o * kSortBlock + tid];
+    ob[tid + kSelThreads] = sorted[(int64_t)o * kSortBlock + tid + kSelThreads];
+    __syncthreads();
+    r0 += count_greater(ob, x0);
+    r1 += count_greater(ob, x1);
+  }
+  rank_part[(int64_t)g * npos + j0] = r0;
+  rank_part[(int64_t)g * npos + j1] = r1;
+}
+
+__global__ __launch_bounds__(256) void mt_scatter_kernel(const uint64_t *sorted,
+                                                         const uint32_t *rank_part,
+                                                         int32_t ngroups, int32_t npos,
+                                                         int32_t V, int32_t V_high,
+                                                         int32_t *t2f, int32_t *f2t,
+                                                         const MtState *st, uint64_t *sel_out,
+                                                         uint64_t *tot_out) {
+  const int32_t j = blockIdx.x * 256 + threadIdx.x;
+  if (j < npos) {
+    const uint64_t key = sorted[j];
+    if (key != 0) {  // not a pad
+      uint32_t r = 0;
+      for (int g = 0; g < ngroups; ++g) r += rank_part[(int64_t)g * npos + j];
+      const int32_t id = (int32_t)(~(uint32_t)key);
+      if (r < (uint32_t)V_high) {
+        t2f[r] = id;
+        if (f2t && (uint32_t)id < (uint32_t)V) f2t[id] = (int32_t)r;
+      }
+    }
+  }
+  if (j == 0) {
+    *sel_out = st->sel;
+    *tot_out = st->tot;
+  }
+}
+
+struct MtPlan {
+  int32_t nb, group, ngroups;
+  size_t off_hist, off_comp, off_sorted, off_rank, bytes;
+};
+
+MtPlan mt_plan(int32_t V_high) {
+  MtPlan p;
+  p.nb = (V_high + kSortBlock - 1) / kSortBlock;
+  p.group = std::max(kRankGroup, (p.nb + kRankGroupsMax - 1) / kRankGroupsMax);
+  p.ngroups = (p.nb + p.group - 1) / p.group;
+  size_t off = align_up(sizeof(MtState), 256);
+  p.off_hist = off;
+  off += align_up(2048 * 4, 256);
+  p.off_comp = off;
+  off += align_up((size_t)V_high * 8, 256);
+  p.off_sorted = off;
+  off += align_up((size_t)p.nb * kSortBlock * 8, 256);
+  p.off_rank = off;
+  off += align_up((size_t)p.ngroups * p.nb * kSortBlock * 4, 256);
+  p.bytes = off;
+  return p;
+}
+
+// One workgroup does the whole selection up to this many ids; past it the
+// many-workgroup path is faster.
+constexpr int32_t kMtMinV = 16384;
+
 }  // namespace
 
 size_t select_ws_bytes(int32_t V, int32_t V_high) {
-  (void)V;
+  if (V >= kMtMinV) return mt_plan(V_high).bytes;
   return 2 * align_up((size_t)V_high * 8, 256);
 }
 
 hipError_t launch_select(const uint32_t *counts, int32_t V, int32_t V_high,
                          int32_t *t2f, int32_t *f2t, uint64_t *sel,
                          uint64_t *tot, void *ws, hipStream_t stream) {
-  uint64_t *a = static_cast<uint64_t *>(ws);
-  uint64_t *b = reinterpret_cast<uint64_t *>(static_cast<char *>(ws) +
-                                             align_up((size_t)V_high * 8, 256));
-  hipLaunchKernelGGL(select_kernel, dim3(1), dim3(kSelThreads), 0, stream,
-                     counts, V, V_high, t2f, f2t, sel, tot, a, b);
+  if (V < kMtMinV) {
+    uint64_t *a = static_cast<uint64_t *>(ws);
+    uint64_t *b = reinterpret_cast<uint64_t *>(static_cast<char *>(ws) +
+                                               align_up((size_t)V_high * 8, 256));
+    hipLaunchKernelGGL(select_kernel, dim3(1), dim3(kSelThreads), 0, stream,
+                       counts, V, V_high, t2f, f2t, sel, tot, a, b);
+    return hipGetLastError();
+  }
+  const MtPlan p = mt_plan(V_high);
+  char *base = static_cast<char *>(ws);
+  MtState *st = reinterpret_cast<MtState *>(base);
+  uint32_t *ghist = reinterpret_cast<uint32_t *>(base + p.off_hist);
+  uint64_t *comp = reinterpret_cast<uint64_t *>(base + p.off_comp);
+  uint64_t *sorted = reinterpret_cast<uint64_t *>(base + p.off_sorted);
+  uint32_t *rank_part = reinterpret_cast<uint32_t *>(base + p.off_rank);
+  const int32_t init_n = std::max(std::max(V, V_high), 2048);
+  hipLaunchKernelGGL(mt_init_kernel, dim3((init_n + 255) / 256), dim3(256), 0, stream, st, ghist,
+                     V_high, f2t, V);
+  const int32_t wgs = (int32_t)(((int64_t)V + 4 * kSelThreads - 1) / (4 * kSelThreads));
+  for (int pass = 0; pass < kPasses; ++pass)
+    hipLaunchKernelGGL(mt_hist_kernel, dim3(wgs), dim3(kSelThreads), 0, stream, counts, V, st,
+                       ghist, pass);
+  hipLaunchKernelGGL(mt_compact_kernel, dim3(wgs), dim3(kSelThreads), 0, stream, counts, V, st,
+                     comp);
+  hipLaunchKernelGGL(mt_block_sort_kernel, dim3(p.nb), dim3(kSelThreads), 0, stream, comp,
+                     V_high, sorted);
+  hipLaunchKernelGGL(mt_rank_kernel, dim3(p.nb * p.ngroups), dim3(kSelThreads), 0, stream,
+                     sorted, p.nb, p.ngroups, p.group, rank_part);
+  const int32_t npos = p.nb * kSortBlock;
+  hipLaunchKernelGGL(mt_scatter_kernel, dim3((npos + 255) / 256), dim3(256), 0, stream, sorted,
+                     rank_part, p.ngroups, npos, V, V_high, t2f, f2t, st, sel, tot);
   return hipGetLastError();
 }
 

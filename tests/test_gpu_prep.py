@@ -116,6 +116,20 @@ def test_select_edge_counts(dlh):
         check_select(dlh, big, V_high)
 
 
+@pytest.mark.parametrize("V", [16384, 16387, 50001])
+def test_select_many_workgroups_edges(dlh, V):
+    # From 16384 ids on the selection runs over many workgroups: all-zero and
+    # uniform counts (pure id order), full-range 32-bit counts, a few maximal
+    # counts over a sea of ties; cuts at and around the 2048-key sort blocks.
+    rng = np.random.default_rng(V)
+    cases = [np.zeros(V, np.uint32), np.full(V, 7, np.uint32),
+             rng.integers(0, 2**32, size=V, dtype=np.uint64).astype(np.uint32),
+             np.where(rng.random(V) < 0.01, 2**32 - 1, rng.integers(0, 3, size=V)).astype(np.uint32)]
+    for c in cases:
+        for V_high in (1, 2, 2047, 2048, 2049, V - 1, V):
+            check_select(dlh, c, V_high)
+
+
 @pytest.mark.parametrize("name", ["llama3_8b", "qwen2_7b"])
 def test_select_full_size(dlh, name):
     w = synth.WORKLOADS[name]
