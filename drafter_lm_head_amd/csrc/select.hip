@@ -500,16 +500,26 @@ __global__ __launch_bounds__(kSelThreads) void mt_block_sort_kernel(const uint64
   for (int i = tid; i < kSortBlock; i += kSelThreads)
     sk[i] = base + i < n ? comp[base + i] : 0ull;
   __syncthreads();
+  // kSortBlock / 2 compare-exchanges per stage, one per thread. Up to a
+  // stride of 64 both keys of every exchange of wave w lie in keys
+  // 128 w .. 128 w + 127, and a wave's LDS accesses are performed in order,
+  // so a workgroup barrier is needed only after a stage that crosses waves
+  // (stride >= 128) or before one (the first stage of a size >= 256).
   for (uint32_t size = 2; size <= (uint32_t)kSortBlock; size <<= 1)
     for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
-      const uint32_t i = tid;  // kSortBlock / 2 compare-exchanges, one per thread
+      const uint32_t i = tid;
       const uint32_t lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
       const uint64_t x = sk[lo], y = sk[hi];
       if ((x < y) == ((lo & size) == 0)) {
         sk[lo] = y;
         sk[hi] = x;
       }
-      __syncthreads();
+      if (stride > (uint32_t)kWave || (stride == 1 && size >= 2 * kWave)) {
+        __syncthreads();
+      } else {
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+      }
     }
   for (int i = tid; i < kSortBlock; i += kSelThreads) sorted[base + i] = sk[i];
 }
