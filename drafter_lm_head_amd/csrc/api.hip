@@ -49,7 +49,7 @@ int vt_version(void) { return VT_ABI_VERSION; }
 size_t vt_count_freq_workspace_size(uint64_t n, int32_t V) {
   if (V <= 0) return 0;
   const vt::CountPlan p = vt::count_plan(n, V);
-  return p.partial_bytes + p.inv_bytes;
+  return p.partial_bytes + p.inv_bytes + p.spill_bytes;
 }
 
 int vt_count_freq(const int32_t *ids, uint64_t n, int32_t V, uint32_t *counts,

@@ -14,12 +14,16 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // gfx950 has 160 KB of LDS per CU; one counting workgroup uses up to
 // kRangeBinsMax 32-bit bins of it.
 constexpr int kRangeBinsMax = 38912;  // 152 KB
+constexpr int kRange16Max = 76800;    // 16-bit bins: 150 KB
+constexpr int kSpillCap = 1024;       // overflow records per 16-bit workgroup
 constexpr int kMaxChunks = 64;        // rows of the partial histogram table
 
 struct CountPlan {
   int32_t n_ranges, range_bins, n_chunks;
   uint64_t chunk_len;
-  size_t partial_bytes, inv_bytes;
+  bool bins16;              // 16-bit LDS bins (vocabularies past kRangeBinsMax ids)
+  int32_t row_pitch;        // partial-table row length in bins
+  size_t partial_bytes, inv_bytes, spill_bytes;
 };
 CountPlan count_plan(uint64_t n, int32_t V);
 hipError_t launch_count(const int32_t *ids, uint64_t n, int32_t V,

@@ -57,7 +57,7 @@ def test_count_small(dlh, case):
 
 def test_count_accumulate(dlh):
     rng = np.random.default_rng(12)
-    V = 40000          # two LDS ranges
+    V = 40000          # one range of 16-bit bins
     a = rng.integers(-5, V + 5, size=123_457).astype(np.int32)
     b = rng.integers(0, V, size=70_001).astype(np.int32)
     c, inv = dlh.vt_count_freq(to_dev_i32(a), V)
@@ -70,13 +70,28 @@ def test_count_accumulate(dlh):
 
 @pytest.mark.parametrize("name", ["llama3_8b", "qwen2_7b"])
 def test_count_full_size(dlh, name):
-    # 1e8 Zipf ids over 128256 / 152064 ids: four LDS ranges, hot bins.
+    # 1e8 Zipf ids over 128256 / 152064 ids: two ranges of 16-bit bins, hot bins.
     w = synth.WORKLOADS[name]
     ids = synth.make_ids(w)
     c, inv = run_count(dlh, ids, w.V)
     c_o, inv_o = oracle.count(ids, w.V)
     np.testing.assert_array_equal(c, c_o)
     assert inv == inv_o == 0
+
+
+@pytest.mark.parametrize("V,n,hot", [(100_000, 20_000_000, 0.9), (152_064, 3_000_001, 0.5),
+                                     (38_913, 1_000_003, 1.0)])
+def test_count_16bit_bins_overflow(dlh, V, n, hot):
+    # Past 38912 ids the counts live in 16-bit LDS bins: a hot id crosses 2^15
+    # many times in every workgroup, so its overflow records carry most of its
+    # count; an odd V puts the hot id next to the padding bin.
+    rng = np.random.default_rng(V)
+    ids = rng.integers(-3, V + 3, size=n).astype(np.int32)
+    ids[rng.random(n) < hot] = V - 1 if V % 2 else V // 2
+    c, inv = run_count(dlh, ids, V)
+    c_o, inv_o = oracle.count(ids, V)
+    np.testing.assert_array_equal(c, c_o)
+    assert inv == inv_o
 
 
 def run_select(dlh, counts, V_high):
