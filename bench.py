@@ -297,7 +297,8 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic() if (w.name == "llama3_8b" and M == 1) else None,
                      "kernel": "head_gemv_kernel" if M <= 2 else
-                               "h_pack_kernel + head_mfma_kernel + head_merge_kernel",
+                               ("head_mfma_kernel + tree_merge_kernel" if M <= 32 else
+                                "h_pack_kernel + head_mfma_kernel + tree_merge_kernel"),
                      "bytes_per_launch": nb,
                      "us_per_launch": round(ms_step * 1000, 3),
                      "us_single_launch_events": round(us_launch, 3)},
