@@ -255,8 +255,41 @@ __device__ void sample_merge(const HeadArgs &a, int m, MergeShared<WAVES> &sh) {
   __syncthreads();  // sh is reused by the next draft row's merge
 }
 
+// Buffer resource over the `count` 8-byte values at p, rounded up to whole
+// 16-byte pairs (every such array of the workspace is followed by another
+// one, so the rounding stays inside it), whose loads are agent-coherent
+// (the sc1 cache policy, as the agent-scope atomic loads of fetch_u64) so
+// that 16-byte loads can read data published by other XCDs. Pairs past the
+// end read as 0; load_pair clears the value past `count` in the last pair.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const uint64_t *p, int count) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint64_t *>(p), 0, (count + 1) / 2 * 16,
+                                           0x00020000);
+}
+constexpr int kCpolSc1 = 16;  // cache policy bit sc1 of buffer loads (gfx940 and later)
+__device__ __forceinline__ void load_pair(__amdgpu_buffer_rsrc_t r, int pair, int count,
+                                          uint64_t &x, uint64_t &y) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, pair * 16, 0, kCpolSc1);
+  x = ((uint64_t)v.y << 32) | v.x;
+  y = 2 * pair + 1 < count ? ((uint64_t)v.w << 32) | v.z : 0ull;
+}
+
+// Final merge over the published tile partials of draft row m, by the last
+// workgroup. Every instruction of every wave costs issue time on the CU's
+// four SIMDs and every load instruction costs issue time in its memory
+// pipeline whether or not any lane is active, so the loops run over the
+// real counts (uniform bounds) and each value is handled once:
+//   * loads: the keys, the tile softmax partials and the group maxima, all
+//     in flight together;
+//   * each wave folds its tile partials into one (max, sum) relative to its
+//     own max; wave 0 ranks the 64 group maxima (the k-th largest of them,
+//     or the largest tile k-th key, bounds the k-th largest key from below);
+//   * after one barrier every wave appends its keys at or above the bound
+//     to the survivors; after a second, wave 0 combines the softmax
+//     partials in a fixed order and ranks the survivors.
 template <int WAVES>
-__device__ void final_merge(const HeadArgs &a, int m, MergeShared<WAVES> &sh) {
+__device__ void final_merge(const HeadArgs &a, int m, MergeShared<WAVES> &sh, bool last) {
+  typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
   constexpr int NT = WAVES * kWave;
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
   const int k = a.k, tiles = a.tiles;
@@ -266,96 +299,143 @@ __device__ void final_merge(const HeadArgs &a, int m, MergeShared<WAVES> &sh) {
   uint64_t *gkth = a.group_kth + (size_t)m * kGroups;
   const int n = tiles * k;
 
-  // One round of loads: two batches of keys, the tile softmax partials and
-  // the group maxima.
-  constexpr int kBatch = 8;
-  uint64_t kb[2][kBatch];
+  // Keys and tile partials in pairs (16-byte agent-coherent loads; pairs
+  // past the end read as 0): key pair j of this thread holds keys
+  // 2 (tid + j NT) and 2 (tid + j NT) + 1.
+  constexpr int kKpp = 8;                              // key pairs per thread in registers
+  constexpr int kTpp = (kMaxTiles / 2 + NT - 1) / NT;  // tile pairs per thread, at most
+  const int kpp = min(kKpp, (n / 2 + 1 + NT - 1) / NT), tpp = (tiles / 2 + 1 + NT - 1) / NT;
+  const __amdgpu_buffer_rsrc_t krs = coherent_rsrc(keys, n);
+  const __amdgpu_buffer_rsrc_t mrs = coherent_rsrc(ms, tiles);
+  uint64_t kb[2 * kKpp], mst[2 * kTpp];
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+  for (int j = 0; j < kKpp; ++j) {
+    kb[2 * j] = kb[2 * j + 1] = 0ull;
+    if (j < kpp) load_pair(krs, tid + j * NT, n, kb[2 * j], kb[2 * j + 1]);
+  }
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int f = tid + (b * kBatch + j) * NT;
-      kb[b][j] = f < n ? fetch_u64(keys + f) : 0ull;
-    }
-  constexpr int kTpt = (kMaxTiles + NT - 1) / NT;  // tiles per thread
-  uint64_t mst[kTpt];
-#pragma unroll
-  for (int j = 0; j < kTpt; ++j) {
-    const int t = tid + j * NT;
-    mst[j] = t < tiles ? fetch_u64(ms + t) : 0ull;
+  for (int j = 0; j < kTpp; ++j) {
+    mst[2 * j] = mst[2 * j + 1] = 0ull;
+    if (j < tpp) load_pair(mrs, tid + j * NT, tiles, mst[2 * j], mst[2 * j + 1]);
   }
   uint64_t g = 0, gk = 0;
   if (wave == 0) {
     g = fetch_u64(gmax + lane);
     gk = fetch_u64(gkth + lane);
   }
+  // This wave's softmax partial, relative to its own max.
+  // (tile partials past the end read as 0: max 0.0, sum 0, so they add 0)
   float mu_l = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < kTpt; ++j)
-    if (tid + j * NT < tiles) mu_l = fmaxf(mu_l, ms_max(mst[j]));
+  for (int j = 0; j < 2 * kTpp; ++j)
+    if (j < 2 * tpp && 2 * (tid + (j / 2) * NT) + (j % 2) < tiles) mu_l = fmaxf(mu_l, ms_max(mst[j]));
   const float mu_w = wave_max(mu_l);
+  float s_l = 0.f;
+#pragma unroll
+  for (int j = 0; j < 2 * kTpp; ++j)
+    if (j < 2 * tpp && 2 * (tid + (j / 2) * NT) + (j % 2) < tiles)
+      s_l += ms_sum(mst[j]) * __expf(ms_max(mst[j]) - mu_w);
+  const float s_w = wave_sum(s_l);
+  if (lane == 0) {
+    sh.f[wave] = mu_w;
+    sh.f2[wave] = s_w;
+  }
   if (wave == 0) {
+    // Rank of each group maximum among the 64 (this wave's own LDS writes).
     sh.sc[0][lane] = g;
-    sh.kmax = wave_max_u64(gk);
-  }
-  if (lane == 0) sh.f[wave] = mu_w;
-  if (tid == 0) sh.cnt = 0;
-  __syncthreads();
-  float mu = sh.f[0];
-  for (int w = 1; w < WAVES; ++w) mu = fmaxf(mu, sh.f[w]);
-  {
-    const uint32_t r = block_rank<WAVES, 1>(sh.sc[0], &sh.prank[0][0][0]);
-    if (wave == 0) {
-      const uint64_t hit = __ballot(r == (uint32_t)(k - 1) && g != 0ull);
-      if (lane == 0) sh.T = max_u64(hit ? readlane_u64(g, __builtin_ctzll(hit)) : 0ull, sh.kmax);
+    // The reads below go through another type: keep them after the write
+    // (compiler barrier) and wait for the write (LDS counter only).
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __asm__ __volatile__("" ::: "memory");
+    uint32_t r = 0;
+#pragma unroll
+    for (int j = 0; j < kWave; j += 2) {
+      const u64x2 q = *reinterpret_cast<const u64x2 *>(sh.sc[0] + j);
+      r += q.x > g;
+      r += q.y > g;
     }
-  }
-  __syncthreads();  // all reads of sh.f done, T ready
-  if (wave == 0) {  // g and gk are in registers: reset the maxima for the next call
+    const uint64_t hit = __ballot(r == (uint32_t)(k - 1) && g != 0ull);
+    const uint64_t T = max_u64(hit ? readlane_u64(g, __builtin_ctzll(hit)) : 0ull, wave_max_u64(gk));
+    if (lane == 0) {
+      sh.T = T;
+      sh.cnt = 0;
+    }
+    // g and gk are in registers: reset the maxima for the next call
     publish_u64(gmax + lane, 0ull);
     publish_u64(gkth + lane, 0ull);
   }
-  float s_l = 0.f;
-#pragma unroll
-  for (int j = 0; j < kTpt; ++j)
-    if (tid + j * NT < tiles) s_l += ms_sum(mst[j]) * __expf(ms_max(mst[j]) - mu);
-  const float s_w = wave_sum(s_l);
-  if (lane == 0) sh.f[wave] = s_w;
+  if (wave == 1) sh.cand[lane] = 0;  // up to 64 survivors are ranked over 64 slots
+  __syncthreads();
   const uint64_t T = sh.T;
+  auto offer_wave = [&](uint64_t v) {
+    const bool keep = v != 0ull && v >= T;
+    const uint64_t mask = __ballot(keep);
+    if (mask) {
+      const int first = __builtin_ctzll(mask);
+      uint32_t base = 0;
+      if (lane == first) base = atomicAdd(&sh.cnt, (uint32_t)__builtin_popcountll(mask));
+      base = __builtin_amdgcn_readlane(base, first);
+      const uint32_t pos =
+          base + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+      if (keep && pos < (uint32_t)kCandCap) sh.cand[pos] = v;
+    }
+  };
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+  for (int j = 0; j < 2 * kKpp; ++j)
+    if (j / 2 < kpp) offer_wave(kb[j]);
+  for (int base = kKpp * NT; 2 * base < n; base += kKpp * NT) {  // large k: more passes
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) offer(kb[b][j], T, sh.cand, &sh.cnt);
-  for (int base = 2 * kBatch * NT; base < n; base += kBatch * NT) {
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int f = base + tid + j * NT;
-      kb[0][j] = f < n ? fetch_u64(keys + f) : 0ull;
+    for (int j = 0; j < kKpp; ++j) {
+      kb[2 * j] = kb[2 * j + 1] = 0ull;
+      if (2 * (base + j * NT) < n) load_pair(krs, base + tid + j * NT, n, kb[2 * j], kb[2 * j + 1]);
     }
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) offer(kb[0][j], T, sh.cand, &sh.cnt);
+    for (int j = 0; j < 2 * kKpp; ++j)
+      if (2 * (base + (j / 2) * NT) < n) offer_wave(kb[j]);
   }
   __syncthreads();
   const uint32_t found = sh.cnt;
-  float S = sh.f[0];
-  for (int w = 1; w < WAVES; ++w) S += sh.f[w];
-  uint64_t key = 0;  // rank `tid` for tid < k
+  float mu = sh.f[0];
+#pragma unroll
+  for (int w = 1; w < WAVES; ++w) mu = fmaxf(mu, sh.f[w]);
+  float S = 0.f;
+#pragma unroll
+  for (int w = 0; w < WAVES; ++w)
+    if (sh.f[w] != -INFINITY) S += sh.f2[w] * __expf(sh.f[w] - mu);
   if (found <= (uint32_t)kWave) {
-    // Wave 0 ranks the few survivors against each other (a loop over the
-    // survivors only) and writes each one to its output slot; at least k
-    // keys survive because T is at most the k-th largest key.
+    // Wave 0 ranks the few survivors against each other (the 64 slots past
+    // the survivors hold 0) and writes each one to its output slot; at
+    // least k keys survive because T is at most the k-th largest key.
     if (wave == 0) {
-      const uint64_t v = lane < (int)found ? sh.cand[lane] : 0ull;
+      const uint64_t v = sh.cand[lane];
       uint32_t r = 0;
-      for (uint32_t j = 0; j < found; ++j) r += sh.cand[j] > v;
+      if (found <= 16) {
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) {
+          const u64x2 q = *reinterpret_cast<const u64x2 *>(sh.cand + j);
+          r += q.x > v;
+          r += q.y > v;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kWave; j += 2) {
+          const u64x2 q = *reinterpret_cast<const u64x2 *>(sh.cand + j);
+          r += q.x > v;
+          r += q.y > v;
+        }
+      }
       if (lane < (int)found && r < (uint32_t)k) {
         a.full_ids[(size_t)m * k + r] = key_id(v);
         a.probs[(size_t)m * k + r] = __expf(key_logit(v) - mu) / S;
       }
     }
-    __syncthreads();  // sh is reused by the next draft row's merge
+    if (!last) __syncthreads();  // sh is reused by the next draft row's merge
     return;
-  } else if (found <= (uint32_t)kCandCap) {
+  }
+  uint64_t key = 0;  // rank `tid` for tid < k
+  if (found <= (uint32_t)kCandCap) {
     block_sort_desc<WAVES>(sh.cand, found);
     if (wave == 0) key = sh.cand[lane];
   } else {
@@ -384,10 +464,21 @@ __device__ void final_merge(const HeadArgs &a, int m, MergeShared<WAVES> &sh) {
   __syncthreads();
 }
 
-// GEMV workgroups: 8 waves, one row per wave and step; the W loads of a
-// step (CPL 16-byte chunks per lane) are all in flight at once, and two
-// workgroups per CU (16 waves) keep enough rows in flight.
-constexpr int kGemvWaves = 8;
+// GEMV workgroups. Within a CU the memory pipeline serves the oldest waves
+// first, so of two workgroups sharing a CU one finishes long before the
+// other, and for the rest of the call that CU has half as many rows in
+// flight; the XCDs then no longer get equal shares of the bandwidth, and
+// two or three of them finish several microseconds after the others. A CU
+// therefore runs one workgroup of 16 waves over a block of two 64-row tiles,
+// and its waves take the block's rows one at a time from an LDS counter, so
+// that all 16 keep loading until the block's rows run out. Where 16 waves
+// would not fit in the registers (long rows with two draft rows) the
+// workgroups have 8 waves and one tile each. Each tile's partial (top-k keys,
+// softmax partial) is published as before.
+template <int MT, int CPL>
+constexpr int gemv_waves() {
+  return (CPL <= 8 || (MT == 1 && CPL <= 12)) ? 16 : 8;
+}
 
 template <int WAVES, int MT, int CPL, bool RAGGED, bool LOGITS>
 __global__ __launch_bounds__(WAVES *kWave) void head_gemv_kernel(HeadArgs a) {
@@ -395,18 +486,29 @@ __global__ __launch_bounds__(WAVES *kWave) void head_gemv_kernel(HeadArgs a) {
   // that about 8 loads per lane are in flight; from 6 loads per row on, one
   // row per step measured best.
   constexpr int U = CPL >= 6 ? 1 : CPL >= 3 ? 2 : CPL == 2 ? 4 : 8;
-  static_assert(kTileRows % (WAVES * U) == 0, "tile must split evenly");
-  static_assert(MT <= WAVES, "one wave per draft row in the epilogue");
-  __shared__ float s_z[MT][kTileRows];
+  constexpr int kTiles = WAVES / 8;            // 64-row tiles per workgroup
+  constexpr int kRows = kTiles * kTileRows;
+  static_assert(kRows % U == 0, "units must split the block evenly");
+  static_assert(kTiles * MT <= WAVES, "one wave per (tile, draft row) in the epilogue");
+  __shared__ float s_z[MT][kRows];
   __shared__ MergeShared<WAVES> sh;
-  __shared__ uint32_t s_slot;
+  __shared__ uint32_t s_slot, s_next;
 
   const int lane = __lane_id(), wave = threadIdx.x / kWave;
-  const int tile = blockIdx.x, row0 = tile * kTileRows;
+  const int tile0 = blockIdx.x * kTiles, row0 = tile0 * kTileRows;
   const int c16 = a.c16;
+  // Units of U rows in this block (the last block may be short).
+  const int units = (min(kRows, a.V_high - row0) + U - 1) / U;
 
+  // Epilogue roles: wave e = sub * MT + m takes tile tile0 + sub, draft row m.
+  const int e_sub = wave / MT, e_m = wave % MT;
+  const bool e_on = wave < kTiles * MT && tile0 + e_sub < a.tiles;
+  const int e_row = row0 + e_sub * kTileRows + lane;
   int32_t fid = 0;
-  if (!LOGITS && wave < MT && row0 + lane < a.V_high) fid = a.t2f[row0 + lane];
+  if (!LOGITS && e_on && e_row < a.V_high) fid = a.t2f[e_row];
+
+  if (threadIdx.x == 0) s_next = WAVES;  // unit w < WAVES is wave w's first
+  __syncthreads();
 
   u32x4 hr[MT][CPL];
 #pragma unroll
@@ -418,10 +520,9 @@ __global__ __launch_bounds__(WAVES *kWave) void head_gemv_kernel(HeadArgs a) {
                                         : u32x4{0, 0, 0, 0};
     }
 
-  constexpr int kSteps = kTileRows / (WAVES * U);
 #pragma unroll 1
-  for (int s = 0; s < kSteps; ++s) {
-    const int rl = (s * WAVES + wave) * U;  // first tile-local row of the wave
+  for (int u0 = wave; u0 < units;) {
+    const int rl = u0 * U;  // first block-local row of the unit
     u32x4 w[U][CPL];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -453,6 +554,7 @@ __global__ __launch_bounds__(WAVES *kWave) void head_gemv_kernel(HeadArgs a) {
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int m = 0; m < MT; ++m) z[m][u] = wave_sum(z[m][u]);
+    uint32_t next = 0;
     if (lane == 0) {
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -465,62 +567,67 @@ __global__ __launch_bounds__(WAVES *kWave) void head_gemv_kernel(HeadArgs a) {
             s_z[m][rl + u] = z[m][u];
           }
         }
+      next = atomicAdd(&s_next, 1u);
     }
+    u0 = (int)__builtin_amdgcn_readfirstlane(next);
   }
   if (LOGITS) return;
   __syncthreads();
 
-  const bool valid = row0 + lane < a.V_high;
-  // Wave m < MT works on draft row m: its logit of tile row `lane`, with the
-  // head's bias when it has one.
+  const int tile = tile0 + e_sub;
+  const bool valid = e_on && e_row < a.V_high;
+  // Wave e works on draft row e_m of tile `tile`: its logit of tile row
+  // `lane`, with the head's bias when it has one.
   float zl = 0.f;
-  if (wave < MT) {
-    zl = s_z[wave][lane];
-    if (a.bias && valid) zl += bf16_to_f32(a.bias[row0 + lane]);
+  if (e_on) {
+    zl = s_z[e_m][e_sub * kTileRows + lane];
+    if (a.bias && valid) zl += bf16_to_f32(a.bias[e_row]);
   }
   if (a.sample) {  // one draw per draft row
-    if (wave < MT)
-      wave_publish_sample(a, wave, tile, zl,
-                          gumbel(a.seed_lo, a.seed_hi, a.off_lo, a.off_hi, wave, row0 + lane),
+    if (e_on)
+      wave_publish_sample(a, e_m, tile, zl,
+                          gumbel(a.seed_lo, a.seed_hi, a.off_lo, a.off_hi, e_m, e_row),
                           fid, valid);
-    if (arrive(a.counter, &s_slot) != (uint32_t)(a.tiles - 1)) return;
+    if (arrive(a.counter, &s_slot) != gridDim.x - 1) return;
     for (int m = 0; m < MT; ++m) sample_merge<WAVES>(a, m, sh);
     if (threadIdx.x == 0) reset_counter(a.counter);
     return;
   }
 
-  // Tile partial: top-k keys and softmax partial of each draft row.
+  // Tile partials: top-k keys and softmax partial of each (tile, draft row).
+  constexpr int NR = kTiles * MT;
   const int k = a.k;
-  uint64_t *s_key = sh.cand;               // [MT][64] keys of the tile
-  uint64_t *s_top = sh.cand + MT * kWave;  // [MT][64] ranked keys
-  if (wave < MT) {
+  uint64_t *s_key = sh.cand;               // [NR][64] keys of the tiles
+  uint64_t *s_top = sh.cand + NR * kWave;  // [NR][64] ranked keys
+  if (wave < NR) {
     s_key[wave * kWave + lane] = valid ? make_key(zl, fid) : 0ull;
     s_top[wave * kWave + lane] = 0;
   }
   __syncthreads();
-  const uint32_t rank = block_rank<WAVES, MT>(s_key, &sh.prank[0][0][0]);
-  if (wave < MT) {
-    const int m = wave;
-    if (rank < (uint32_t)k) s_top[m * kWave + rank] = s_key[m * kWave + lane];
+  const uint32_t rank = block_rank<WAVES, NR>(s_key, &sh.prank[0][0][0]);
+  if (e_on) {
+    const int m = e_m;
+    if (rank < (uint32_t)k) s_top[wave * kWave + rank] = s_key[wave * kWave + lane];
     __builtin_amdgcn_wave_barrier();
-    const uint64_t key = s_top[m * kWave + lane];
-    const float mu = key_logit(s_top[m * kWave]);
+    const uint64_t key = s_top[wave * kWave + lane];
+    const float mu = key_logit(s_top[wave * kWave]);
     const float S = wave_sum(valid ? __expf(zl - mu) : 0.f);
     if (lane < k) publish_u64(a.tile_keys + ((size_t)m * a.tiles + tile) * k + lane, key);
     if (lane == 0) {
       publish_u64(a.tile_ms + (size_t)m * a.tiles + tile, pack_ms(mu, S));
       const int grp = tile / a.tiles_per_group;
       __hip_atomic_fetch_max(a.group_max + (size_t)m * kGroups + grp,
-                             s_top[m * kWave], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                             s_top[wave * kWave], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_fetch_max(a.group_kth + (size_t)m * kGroups + grp,
-                             s_top[m * kWave + k - 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                             s_top[wave * kWave + k - 1], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 
-  // The last tile to finish merges every tile's partial.
-  if (arrive(a.counter, &s_slot) != (uint32_t)(a.tiles - 1)) return;
-  for (int m = 0; m < MT; ++m) final_merge<WAVES>(a, m, sh);
+  // The last workgroup to finish merges every tile's partial.
+  if (arrive(a.counter, &s_slot) != gridDim.x - 1) return;
   if (threadIdx.x == 0) reset_counter(a.counter);
+  for (int m = 0; m < MT; ++m) final_merge<WAVES>(a, m, sh, m == MT - 1);
 }
 
 // ---------------------------------------------------------------- MFMA path
@@ -933,9 +1040,10 @@ constexpr int kCplSet[] = {1, 2, 3, 4, 5, 6, 7, 8, 12, 16};
 
 template <int MT, bool LOGITS, int CPL, bool RAGGED>
 hipError_t launch_one(const HeadArgs &a, hipStream_t stream) {
-  constexpr int WAVES = kGemvWaves;
+  constexpr int WAVES = gemv_waves<MT, CPL>();
+  constexpr int kTiles = WAVES / 8;
   hipLaunchKernelGGL((head_gemv_kernel<WAVES, MT, CPL, RAGGED, LOGITS>),
-                     dim3(a.tiles), dim3(WAVES * kWave), 0, stream, a);
+                     dim3((a.tiles + kTiles - 1) / kTiles), dim3(WAVES * kWave), 0, stream, a);
   return hipGetLastError();
 }
 
