@@ -189,19 +189,24 @@ __device__ void sample_merge(const HeadArgs &a, int m, MergeShared<WAVES> &sh) {
   const uint64_t *keys = a.tile_keys + (size_t)m * tiles;
   const uint64_t *zs = a.tile_z + (size_t)m * tiles;
   const uint64_t *ms = a.tile_ms + (size_t)m * tiles;
-  uint64_t best = 0;
-  float zb = 0.f, mu_l = -INFINITY;
-  // The thread's tiles in index order: keys, their z, softmax partials.
+  // The thread's tiles t = tid + j NT in index order (uniform bound on j):
+  // keys and their z, and the softmax partials, relative to the thread's
+  // own max and then to the wave's.
   constexpr int kB = 4;
-  uint64_t ms_keep[kB];
-  for (int base = 0; base < tiles; base += kB * NT) {
-    uint64_t kv[kB], zv[kB];
+  const int tpt = (tiles + NT - 1) / NT;
+  uint64_t best = 0;
+  float zb = 0.f, mu_l = -INFINITY, s_l = 0.f;
+  for (int base = 0; base < tpt; base += kB) {
+    uint64_t kv[kB], zv[kB], mv[kB];
 #pragma unroll
     for (int j = 0; j < kB; ++j) {
-      const int t = base + tid + j * NT;
-      kv[j] = t < tiles ? fetch_u64(keys + t) : 0ull;
-      zv[j] = t < tiles ? fetch_u64(zs + t) : 0ull;
-      ms_keep[j] = t < tiles ? fetch_u64(ms + t) : 0ull;
+      kv[j] = zv[j] = mv[j] = 0ull;
+      const int t = tid + (base + j) * NT;
+      if (base + j < tpt && t < tiles) {
+        kv[j] = fetch_u64(keys + t);
+        zv[j] = fetch_u64(zs + t);
+        mv[j] = fetch_u64(ms + t);
+      }
     }
 #pragma unroll
     for (int j = 0; j < kB; ++j) {
@@ -209,22 +214,19 @@ __device__ void sample_merge(const HeadArgs &a, int m, MergeShared<WAVES> &sh) {
         best = kv[j];
         zb = __uint_as_float((uint32_t)zv[j]);
       }
-      if (base + tid + j * NT < tiles) mu_l = fmaxf(mu_l, ms_max(ms_keep[j]));
+      if (base + j < tpt && tid + (base + j) * NT < tiles) {
+        const float mj = ms_max(mv[j]);
+        if (mj > mu_l) {
+          s_l = s_l * __expf(mu_l - mj) + ms_sum(mv[j]);
+          mu_l = mj;
+        } else {
+          s_l += ms_sum(mv[j]) * __expf(mj - mu_l);
+        }
+      }
     }
   }
   const float mu_w = wave_max(mu_l);
-  float s_l = 0.f;
-  for (int base = 0; base < tiles; base += kB * NT) {
-    if (tiles > kB * NT)  // more than one round: reload (else still in registers)
-#pragma unroll
-      for (int j = 0; j < kB; ++j) {
-        const int t = base + tid + j * NT;
-        ms_keep[j] = t < tiles ? fetch_u64(ms + t) : 0ull;
-      }
-#pragma unroll
-    for (int j = 0; j < kB; ++j)
-      if (base + tid + j * NT < tiles) s_l += ms_sum(ms_keep[j]) * __expf(ms_max(ms_keep[j]) - mu_w);
-  }
+  if (mu_l != -INFINITY) s_l *= __expf(mu_l - mu_w);
   const float s_w = wave_sum(s_l);
   const uint64_t bw = wave_max_u64(best);
   const uint64_t hit = __ballot(best == bw && bw != 0ull);
