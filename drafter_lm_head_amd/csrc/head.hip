@@ -257,41 +257,19 @@ __device__ void sample_merge(const HeadArgs &a, int m, MergeShared<WAVES> &sh) {
   __syncthreads();  // sh is reused by the next draft row's merge
 }
 
-// Buffer resource over the `count` 8-byte values at p, rounded up to whole
-// 16-byte pairs (every such array of the workspace is followed by another
-// one, so the rounding stays inside it), whose loads are agent-coherent
-// (the sc1 cache policy, as the agent-scope atomic loads of fetch_u64) so
-// that 16-byte loads can read data published by other XCDs. Pairs past the
-// end read as 0; load_pair clears the value past `count` in the last pair.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const uint64_t *p, int count) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint64_t *>(p), 0, (count + 1) / 2 * 16,
-                                           0x00020000);
-}
-constexpr int kCpolSc1 = 16;  // cache policy bit sc1 of buffer loads (gfx940 and later)
-__device__ __forceinline__ void load_pair(__amdgpu_buffer_rsrc_t r, int pair, int count,
-                                          uint64_t &x, uint64_t &y) {
-  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-  const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, pair * 16, 0, kCpolSc1);
-  x = ((uint64_t)v.y << 32) | v.x;
-  y = 2 * pair + 1 < count ? ((uint64_t)v.w << 32) | v.z : 0ull;
-}
-
-// Final merge over the published tile partials of draft row m, by the last
-// workgroup. Every instruction of every wave costs issue time on the CU's
-// four SIMDs and every load instruction costs issue time in its memory
-// pipeline whether or not any lane is active, so the loops run over the
-// real counts (uniform bounds) and each value is handled once:
-//   * loads: the keys, the tile softmax partials and the group maxima, all
-//     in flight together;
-//   * each wave folds its tile partials into one (max, sum) relative to its
-//     own max; wave 0 ranks the 64 group maxima (the k-th largest of them,
-//     or the largest tile k-th key, bounds the k-th largest key from below);
-//   * after one barrier every wave appends its keys at or above the bound
-//     to the survivors; after a second, wave 0 combines the softmax
-//     partials in a fixed order and ranks the survivors.
-template <int WAVES>
-__device__ void final_merge(const HeadArgs &a, int m, MergeShared<WAVES> &sh, bool last) {
-  typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+// Final merge over the published tile partials of draft row m, by the
+// first WAVES waves of the last workgroup (SW waves share its LDS):
+//   * softmax: global max of the tile maxima, then the sum of the tile sums
+//     rescaled to it, in a fixed order (no dependence on timing);
+//   * picks: the k-th largest key overall is at least T, the larger of the
+//     largest tile k-th key and the k-th largest of the 64 tile-group
+//     maxima (both are k-th largest keys of sets of real candidates; the
+//     tiles fold them in with atomic max). Keys >= T, typically a few
+//     dozen, are collected in LDS and ranked. With more than 64 survivors
+//     (exact ties, large k) a workgroup sort or, past kCandCap, k exact
+//     max rounds take over.
+template <int WAVES, int SW>
+__device__ void final_merge(const HeadArgs &a, int m, MergeShared<SW> &sh) {
   constexpr int NT = WAVES * kWave;
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
   const int k = a.k, tiles = a.tiles;
@@ -301,143 +279,96 @@ __device__ void final_merge(const HeadArgs &a, int m, MergeShared<WAVES> &sh, bo
   uint64_t *gkth = a.group_kth + (size_t)m * kGroups;
   const int n = tiles * k;
 
-  // Keys and tile partials in pairs (16-byte agent-coherent loads; pairs
-  // past the end read as 0): key pair j of this thread holds keys
-  // 2 (tid + j NT) and 2 (tid + j NT) + 1.
-  constexpr int kKpp = 8;                              // key pairs per thread in registers
-  constexpr int kTpp = (kMaxTiles / 2 + NT - 1) / NT;  // tile pairs per thread, at most
-  const int kpp = min(kKpp, (n / 2 + 1 + NT - 1) / NT), tpp = (tiles / 2 + 1 + NT - 1) / NT;
-  const __amdgpu_buffer_rsrc_t krs = coherent_rsrc(keys, n);
-  const __amdgpu_buffer_rsrc_t mrs = coherent_rsrc(ms, tiles);
-  uint64_t kb[2 * kKpp], mst[2 * kTpp];
+  // One round of loads: two batches of keys, the tile softmax partials and
+  // the group maxima.
+  constexpr int kBatch = 8;
+  uint64_t kb[2][kBatch];
 #pragma unroll
-  for (int j = 0; j < kKpp; ++j) {
-    kb[2 * j] = kb[2 * j + 1] = 0ull;
-    if (j < kpp) load_pair(krs, tid + j * NT, n, kb[2 * j], kb[2 * j + 1]);
-  }
+  for (int b = 0; b < 2; ++b)
 #pragma unroll
-  for (int j = 0; j < kTpp; ++j) {
-    mst[2 * j] = mst[2 * j + 1] = 0ull;
-    if (j < tpp) load_pair(mrs, tid + j * NT, tiles, mst[2 * j], mst[2 * j + 1]);
+    for (int j = 0; j < kBatch; ++j) {
+      const int f = tid + (b * kBatch + j) * NT;
+      kb[b][j] = f < n ? fetch_u64(keys + f) : 0ull;
+    }
+  constexpr int kTpt = (kMaxTiles + NT - 1) / NT;  // tiles per thread
+  uint64_t mst[kTpt];
+#pragma unroll
+  for (int j = 0; j < kTpt; ++j) {
+    const int t = tid + j * NT;
+    mst[j] = t < tiles ? fetch_u64(ms + t) : 0ull;
   }
   uint64_t g = 0, gk = 0;
   if (wave == 0) {
     g = fetch_u64(gmax + lane);
     gk = fetch_u64(gkth + lane);
   }
-  // This wave's softmax partial, relative to its own max.
-  // (tile partials past the end read as 0: max 0.0, sum 0, so they add 0)
   float mu_l = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < 2 * kTpp; ++j)
-    if (j < 2 * tpp && 2 * (tid + (j / 2) * NT) + (j % 2) < tiles) mu_l = fmaxf(mu_l, ms_max(mst[j]));
+  for (int j = 0; j < kTpt; ++j)
+    if (tid + j * NT < tiles) mu_l = fmaxf(mu_l, ms_max(mst[j]));
   const float mu_w = wave_max(mu_l);
-  float s_l = 0.f;
-#pragma unroll
-  for (int j = 0; j < 2 * kTpp; ++j)
-    if (j < 2 * tpp && 2 * (tid + (j / 2) * NT) + (j % 2) < tiles)
-      s_l += ms_sum(mst[j]) * __expf(ms_max(mst[j]) - mu_w);
-  const float s_w = wave_sum(s_l);
-  if (lane == 0) {
-    sh.f[wave] = mu_w;
-    sh.f2[wave] = s_w;
-  }
   if (wave == 0) {
-    // Rank of each group maximum among the 64 (this wave's own LDS writes).
     sh.sc[0][lane] = g;
-    // The reads below go through another type: keep them after the write
-    // (compiler barrier) and wait for the write (LDS counter only).
-    __asm__ __volatile__("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __asm__ __volatile__("" ::: "memory");
-    uint32_t r = 0;
-#pragma unroll
-    for (int j = 0; j < kWave; j += 2) {
-      const u64x2 q = *reinterpret_cast<const u64x2 *>(sh.sc[0] + j);
-      r += q.x > g;
-      r += q.y > g;
+    sh.kmax = wave_max_u64(gk);
+  }
+  if (lane == 0) sh.f[wave] = mu_w;
+  if (tid == 0) sh.cnt = 0;
+  __syncthreads();
+  float mu = sh.f[0];
+  for (int w = 1; w < WAVES; ++w) mu = fmaxf(mu, sh.f[w]);
+  {
+    const uint32_t r = block_rank<WAVES, 1>(sh.sc[0], &sh.prank[0][0][0]);
+    if (wave == 0) {
+      const uint64_t hit = __ballot(r == (uint32_t)(k - 1) && g != 0ull);
+      if (lane == 0) sh.T = max_u64(hit ? readlane_u64(g, __builtin_ctzll(hit)) : 0ull, sh.kmax);
     }
-    const uint64_t hit = __ballot(r == (uint32_t)(k - 1) && g != 0ull);
-    const uint64_t T = max_u64(hit ? readlane_u64(g, __builtin_ctzll(hit)) : 0ull, wave_max_u64(gk));
-    if (lane == 0) {
-      sh.T = T;
-      sh.cnt = 0;
-    }
-    // g and gk are in registers: reset the maxima for the next call
+  }
+  __syncthreads();  // all reads of sh.f done, T ready
+  if (wave == 0) {  // g and gk are in registers: reset the maxima for the next call
     publish_u64(gmax + lane, 0ull);
     publish_u64(gkth + lane, 0ull);
   }
-  if (wave == 1) sh.cand[lane] = 0;  // up to 64 survivors are ranked over 64 slots
-  __syncthreads();
+  float s_l = 0.f;
+#pragma unroll
+  for (int j = 0; j < kTpt; ++j)
+    if (tid + j * NT < tiles) s_l += ms_sum(mst[j]) * __expf(ms_max(mst[j]) - mu);
+  const float s_w = wave_sum(s_l);
+  if (lane == 0) sh.f[wave] = s_w;
   const uint64_t T = sh.T;
-  auto offer_wave = [&](uint64_t v) {
-    const bool keep = v != 0ull && v >= T;
-    const uint64_t mask = __ballot(keep);
-    if (mask) {
-      const int first = __builtin_ctzll(mask);
-      uint32_t base = 0;
-      if (lane == first) base = atomicAdd(&sh.cnt, (uint32_t)__builtin_popcountll(mask));
-      base = __builtin_amdgcn_readlane(base, first);
-      const uint32_t pos =
-          base + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-      if (keep && pos < (uint32_t)kCandCap) sh.cand[pos] = v;
-    }
-  };
 #pragma unroll
-  for (int j = 0; j < 2 * kKpp; ++j)
-    if (j / 2 < kpp) offer_wave(kb[j]);
-  for (int base = kKpp * NT; 2 * base < n; base += kKpp * NT) {  // large k: more passes
+  for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int j = 0; j < kKpp; ++j) {
-      kb[2 * j] = kb[2 * j + 1] = 0ull;
-      if (2 * (base + j * NT) < n) load_pair(krs, base + tid + j * NT, n, kb[2 * j], kb[2 * j + 1]);
+    for (int j = 0; j < kBatch; ++j) offer(kb[b][j], T, sh.cand, &sh.cnt);
+  for (int base = 2 * kBatch * NT; base < n; base += kBatch * NT) {
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int f = base + tid + j * NT;
+      kb[0][j] = f < n ? fetch_u64(keys + f) : 0ull;
     }
 #pragma unroll
-    for (int j = 0; j < 2 * kKpp; ++j)
-      if (2 * (base + (j / 2) * NT) < n) offer_wave(kb[j]);
+    for (int j = 0; j < kBatch; ++j) offer(kb[0][j], T, sh.cand, &sh.cnt);
   }
   __syncthreads();
   const uint32_t found = sh.cnt;
-  float mu = sh.f[0];
-#pragma unroll
-  for (int w = 1; w < WAVES; ++w) mu = fmaxf(mu, sh.f[w]);
-  float S = 0.f;
-#pragma unroll
-  for (int w = 0; w < WAVES; ++w)
-    if (sh.f[w] != -INFINITY) S += sh.f2[w] * __expf(sh.f[w] - mu);
+  float S = sh.f[0];
+  for (int w = 1; w < WAVES; ++w) S += sh.f[w];
+  uint64_t key = 0;  // rank `tid` for tid < k
   if (found <= (uint32_t)kWave) {
-    // Wave 0 ranks the few survivors against each other (the 64 slots past
-    // the survivors hold 0) and writes each one to its output slot; at
-    // least k keys survive because T is at most the k-th largest key.
+    // Wave 0 ranks the few survivors against each other (a loop over the
+    // survivors only) and writes each one to its output slot; at least k
+    // keys survive because T is at most the k-th largest key.
     if (wave == 0) {
-      const uint64_t v = sh.cand[lane];
+      const uint64_t v = lane < (int)found ? sh.cand[lane] : 0ull;
       uint32_t r = 0;
-      if (found <= 16) {
-#pragma unroll
-        for (int j = 0; j < 16; j += 2) {
-          const u64x2 q = *reinterpret_cast<const u64x2 *>(sh.cand + j);
-          r += q.x > v;
-          r += q.y > v;
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < kWave; j += 2) {
-          const u64x2 q = *reinterpret_cast<const u64x2 *>(sh.cand + j);
-          r += q.x > v;
-          r += q.y > v;
-        }
-      }
+      for (uint32_t j = 0; j < found; ++j) r += sh.cand[j] > v;
       if (lane < (int)found && r < (uint32_t)k) {
         a.full_ids[(size_t)m * k + r] = key_id(v);
         a.probs[(size_t)m * k + r] = __expf(key_logit(v) - mu) / S;
       }
     }
-    if (!last) __syncthreads();  // sh is reused by the next draft row's merge
+    __syncthreads();  // sh is reused by the next draft row's merge
     return;
-  }
-  uint64_t key = 0;  // rank `tid` for tid < k
-  if (found <= (uint32_t)kCandCap) {
+  } else if (found <= (uint32_t)kCandCap) {
     block_sort_desc<WAVES>(sh.cand, found);
     if (wave == 0) key = sh.cand[lane];
   } else {
@@ -629,7 +560,10 @@ __global__ __launch_bounds__(WAVES *kWave) void head_gemv_kernel(HeadArgs a) {
   // The last workgroup to finish merges every tile's partial.
   if (arrive(a.counter, &s_slot) != gridDim.x - 1) return;
   if (threadIdx.x == 0) reset_counter(a.counter);
-  for (int m = 0; m < MT; ++m) final_merge<WAVES>(a, m, sh, m == MT - 1);
+  // The merge is latency-bound: past 8 waves more waves only add work.
+  constexpr int MW = WAVES < 8 ? WAVES : 8;
+  if (wave >= MW) return;
+  for (int m = 0; m < MT; ++m) final_merge<MW, WAVES>(a, m, sh);
 }
 
 // ---------------------------------------------------------------- MFMA path
@@ -1040,13 +974,24 @@ hipError_t launch_mfma(const HeadArgs &a, hipStream_t stream) {
 // ---------------------------------------------------------------- dispatch
 constexpr int kCplSet[] = {1, 2, 3, 4, 5, 6, 7, 8, 12, 16};
 
-template <int MT, bool LOGITS, int CPL, bool RAGGED>
-hipError_t launch_one(const HeadArgs &a, hipStream_t stream) {
-  constexpr int WAVES = gemv_waves<MT, CPL>();
+// Workgroups of two tiles need 512 tiles to give every CU one; below that
+// one-tile workgroups (two per CU) spread the rows over more CUs.
+constexpr int kWideMinTiles = 512;
+
+template <int WAVES, int MT, bool LOGITS, int CPL, bool RAGGED>
+hipError_t launch_waves(const HeadArgs &a, hipStream_t stream) {
   constexpr int kTiles = WAVES / 8;
   hipLaunchKernelGGL((head_gemv_kernel<WAVES, MT, CPL, RAGGED, LOGITS>),
                      dim3((a.tiles + kTiles - 1) / kTiles), dim3(WAVES * kWave), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int MT, bool LOGITS, int CPL, bool RAGGED>
+hipError_t launch_one(const HeadArgs &a, hipStream_t stream) {
+  constexpr int WIDE = gemv_waves<MT, CPL>();
+  if (WIDE == 16 && a.tiles >= kWideMinTiles)
+    return launch_waves<WIDE, MT, LOGITS, CPL, RAGGED>(a, stream);
+  return launch_waves<8, MT, LOGITS, CPL, RAGGED>(a, stream);
 }
 
 template <int MT, bool LOGITS, int I = 0>

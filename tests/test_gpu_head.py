@@ -92,6 +92,14 @@ def test_hidden_sizes(dlh, d):
     check_case(dlh, h, W, t2f, 10)
 
 
+@pytest.mark.parametrize("d,V_high", [(6144, 777), (8192, 1000), (8192, 65), (4096, 4097)])
+def test_two_rows_long_hidden(dlh, d, V_high):
+    # Two draft rows with long rows: the register budget gives 8-wave
+    # workgroups of one tile (d > 4096) or 16-wave ones of two tiles.
+    h, W, t2f = rand_case(400 + d + V_high, 2, d, V_high)
+    check_case(dlh, h, W, t2f, min(10, V_high))
+
+
 @pytest.mark.parametrize("k", [1, 2, 31, 32, 63, 64])
 def test_k_range(dlh, k):
     h, W, t2f = rand_case(100 + k, 2, 256, 5000, hscale=4.0)
@@ -156,7 +164,7 @@ def test_hand_worked_example(dlh):
     np.testing.assert_allclose(probs_g, np.array(g["probs"]), rtol=2e-6)
 
 
-@pytest.mark.parametrize("M", [3, 20, 200])
+@pytest.mark.parametrize("M", [1, 2, 3, 20, 200])
 def test_determinism_and_counter_reset(dlh, M):
     h, W, t2f = rand_case(7, M, 1024, 20000)
     hd, Wd, td = to_dev_bf16(h), to_dev_bf16(W), to_dev_i32(t2f)
