@@ -100,6 +100,33 @@ def test_two_rows_long_hidden(dlh, d, V_high):
     check_case(dlh, h, W, t2f, min(10, V_high))
 
 
+@pytest.mark.parametrize("V_high,d,M", [(32768, 4096, 1), (32833, 4096, 2), (40000, 2048, 1),
+                                         (32800, 2048, 2), (65536, 1024, 1)])
+def test_large_vocab_tail_rows(dlh, V_high, d, M):
+    # From 512 tiles on, one or two draft rows run two-tile 16-wave
+    # workgroups (ragged last blocks of one tile or a partial one, two-row
+    # units at d = 2048, four-row units at d = 1024).
+    h, W, t2f = rand_case(500 + V_high + d, M, d, V_high, V=V_high + 1000, hscale=2.0)
+    check_case(dlh, h, W, t2f, 10)
+
+
+def test_large_vocab_repeatable(dlh):
+    # Which wave computes a row changes from call to call (rows are taken
+    # from a counter); the results must not.
+    h, W, t2f = rand_case(77, 1, 4096, 32768)
+    hd, Wd, td = to_dev_bf16(h), to_dev_bf16(W), to_dev_i32(t2f)
+    n = dlh.vt_draft_head_workspace_size(1, 32768, 4096, 10)
+    ws = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    ref = None
+    for _ in range(30):
+        ids, probs = dlh.vt_draft_head(hd, Wd, td, 10, ws=ws)
+        cur = (ids.cpu().numpy().tobytes(), probs.cpu().numpy().tobytes())
+        ref = ref or cur
+        assert cur == ref
+    torch.cuda.synchronize()
+    assert int(ws[:256 + 2 * 2 * 64 * 8].to(torch.int64).sum().item()) == 0
+
+
 @pytest.mark.parametrize("k", [1, 2, 31, 32, 63, 64])
 def test_k_range(dlh, k):
     h, W, t2f = rand_case(100 + k, 2, 256, 5000, hscale=4.0)
