@@ -129,7 +129,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the draft head is measured on one "
-              "MI355X; multi-GPU runs are not part of this build", file=sys.stderr)
+              "MI355X; it has no multi-GPU mode", file=sys.stderr)
         sys.exit(2)
 
     import torch

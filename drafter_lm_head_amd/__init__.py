@@ -79,7 +79,7 @@ def lib():
         if _lib is None:
             if not os.path.exists(lib_path):
                 raise RuntimeError(
-                    f"{lib_path} is missing: build it with __graft_entry__.build() "
+                    f"{lib_path} is missing: build it with python -m drafter_lm_head_amd.build "
                     "(hipcc, gfx950); there is no fallback implementation")
             h = C.CDLL(lib_path)
             for name, (res, args) in _SIGS.items():

@@ -36,7 +36,7 @@ const char *vt_status_string(int status) {
   switch (status) {
     case VT_OK: return "ok";
     case VT_ERR_INVALID_ARG: return "invalid argument";
-    case VT_ERR_UNSUPPORTED: return "unsupported size for this build";
+    case VT_ERR_UNSUPPORTED: return "size beyond the library's limits";
     case VT_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case VT_ERR_HIP: return "HIP launch failed";
     default: return "unknown status";

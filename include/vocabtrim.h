@@ -44,7 +44,7 @@ extern "C" {
 
 #define VT_ABI_VERSION 1
 
-/* Limits of this build. */
+/* Limits of the library. */
 #define VT_K_MAX 64           /* top-k per draft row                        */
 #define VT_M_MAX 512          /* draft rows per vt_draft_head call           */
 #define VT_D_MAX 8192         /* hidden size; d must also be a multiple of 8 */
@@ -53,7 +53,7 @@ extern "C" {
 typedef enum {
     VT_OK = 0,
     VT_ERR_INVALID_ARG = -1,  /* null/misaligned pointer or size out of range */
-    VT_ERR_UNSUPPORTED = -2,  /* valid request beyond this build's limits     */
+    VT_ERR_UNSUPPORTED = -2,  /* valid request beyond the library's limits   */
     VT_ERR_WORKSPACE = -3,    /* workspace missing, misaligned or too small   */
     VT_ERR_HIP = -4           /* a HIP launch or query failed                 */
 } vt_status;
