@@ -44,6 +44,7 @@ struct HeadArgs {
   float *probs;          // [M][k]
   float *logits;         // [M][V_high], logits-only variant
   const u32x4 *hp;       // h in MFMA B-operand order (MFMA path)
+  int32_t zstream;       // MFMA path: logits to the workspace with streaming stores
   // Sampling mode (k = 1): the pick is the largest z + Gumbel(seed, offset).
   int32_t sample;
   uint32_t seed_lo, seed_hi, off_lo, off_hi;
@@ -566,6 +567,163 @@ __global__ __launch_bounds__(WAVES *kWave) void head_gemv_kernel(HeadArgs a) {
   for (int m = 0; m < MT; ++m) final_merge<MW, WAVES>(a, m, sh);
 }
 
+// Top-k merge of the MFMA path, one workgroup per draft row m, from the
+// tiles' softmax partials and the logits in the workspace:
+//   * the softmax max and sum over the row come from the tile partials,
+//     combined in a fixed order;
+//   * each tile's max is a logit of that tile, so the k-th largest of the
+//     maxima of 64 disjoint groups of tiles (with multiplicity) is at most
+//     the row's k-th largest logit: only tiles whose max reaches it can hold
+//     a pick, typically k to 2k of them;
+//   * the logits of those tiles at or above the bound become keys in LDS
+//     and are ranked as in the tile merge.
+// The partials and logits were written by an earlier kernel.
+template <int WAVES>
+__device__ void row_merge(const HeadArgs &a, int m, MergeShared<WAVES> &sh, int32_t *s_tiles,
+                          uint32_t &s_ntiles) {
+  constexpr int NT = WAVES * kWave;
+  constexpr int kTpt = (kMaxTiles + NT - 1) / NT;  // tiles per thread
+  constexpr int GS = NT / kWave;                   // threads per tile group
+  static_assert((GS & (GS - 1)) == 0 && GS <= kWave, "group of threads within a wave");
+  const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
+  const int k = a.k, V = a.V_high, tiles = a.tiles;
+  const uint64_t *ms = a.tile_ms + (size_t)m * tiles;
+  const float *zr = a.zbuf + (size_t)m * a.zpitch;
+
+  // Slots past the tile count are skipped by uniform branches (a load
+  // instruction costs issue time even with no lane active).
+  const int tpt = (tiles + NT - 1) / NT;
+  uint64_t mst[kTpt];
+#pragma unroll
+  for (int j = 0; j < kTpt; ++j) {
+    const int t = tid + j * NT;
+    mst[j] = 0ull;
+    if (j < tpt && t < tiles) mst[j] = ms[t];
+  }
+  float mu_l = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kTpt; ++j)
+    if (j < tpt && tid + j * NT < tiles) mu_l = fmaxf(mu_l, ms_max(mst[j]));
+  uint32_t gmx = mu_l == -INFINITY ? 0u : ord_from_f32(mu_l);
+#pragma unroll
+  for (int x = 1; x < GS; x <<= 1) gmx = max(gmx, (uint32_t)__shfl_xor((int)gmx, x));
+  if ((lane & (GS - 1)) == 0) sh.gm[tid / GS] = gmx;
+  const float mw = wave_max(mu_l);
+  if (lane == 0) sh.f[wave] = mw;
+  if (tid == 0) {
+    sh.cnt = 0;
+    s_ntiles = 0;
+  }
+  __syncthreads();
+  float mu = sh.f[0];
+  for (int w = 1; w < WAVES; ++w) mu = fmaxf(mu, sh.f[w]);
+  float s_l = 0.f;
+#pragma unroll
+  for (int j = 0; j < kTpt; ++j)
+    if (j < tpt && tid + j * NT < tiles) s_l += ms_sum(mst[j]) * __expf(ms_max(mst[j]) - mu);
+  const float sw = wave_sum(s_l);
+  if (lane == 0) sh.f2[wave] = sw;
+  if (wave == 0) {
+    // k-th largest of the 64 group maxima: count the larger and the
+    // not-smaller ones with broadcast reads of all 64.
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+    const uint32_t gv = sh.gm[lane];
+    u32x4v q[kWave / 4];
+#pragma unroll
+    for (int j = 0; j < kWave / 4; ++j) q[j] = *reinterpret_cast<const u32x4v *>(&sh.gm[4 * j]);
+    uint32_t gt = 0, ge = 0;
+#pragma unroll
+    for (int j = 0; j < kWave / 4; ++j)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        gt += q[j][c] > gv;
+        ge += q[j][c] >= gv;
+      }
+    const uint64_t hit = __ballot(gt < (uint32_t)k && ge >= (uint32_t)k);
+    if (lane == 0)
+      sh.T = hit ? (uint32_t)__builtin_amdgcn_readlane((int)gv, __builtin_ctzll(hit)) : 0u;
+  }
+  __syncthreads();
+  const uint32_t T = (uint32_t)sh.T;
+  float S = sh.f2[0];
+  for (int w = 1; w < WAVES; ++w) S += sh.f2[w];
+#pragma unroll
+  for (int j = 0; j < kTpt; ++j) {
+    const int t = tid + j * NT;
+    if (j < tpt && t < tiles && ord_from_f32(ms_max(mst[j])) >= T)
+      s_tiles[atomicAdd(&s_ntiles, 1u)] = t;
+  }
+  __syncthreads();
+  const int ne = (int)s_ntiles * kTileRows;  // candidate logits
+  constexpr int kRound = 4;
+  for (int base = 0; base < ne; base += kRound * NT) {
+    float zv[kRound];
+    int jv[kRound];
+#pragma unroll
+    for (int i = 0; i < kRound; ++i) {
+      const int e = base + i * NT + tid;
+      jv[i] = e < ne ? s_tiles[e / kTileRows] * kTileRows + e % kTileRows : V;
+      zv[i] = jv[i] < V ? zr[jv[i]] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < kRound; ++i)
+      if (jv[i] < V && ord_from_f32(zv[i]) >= T) {
+        const uint32_t pos = atomicAdd(&sh.cnt, 1u);
+        if (pos < (uint32_t)kCandCap) sh.cand[pos] = make_key(zv[i], a.t2f[jv[i]]);
+      }
+  }
+  __syncthreads();
+  const uint32_t found = sh.cnt;
+  uint64_t key = 0;  // rank `tid` for tid < k
+  if (found <= (uint32_t)kWave) {
+    if (wave == 0) {
+      const uint64_t x = lane < (int)found ? sh.cand[lane] : 0ull;
+      uint32_t r = 0;
+      for (uint32_t j = 0; j < found; ++j) r += sh.cand[j] > x;
+      if (lane < (int)found && r < (uint32_t)k) {
+        a.full_ids[(size_t)m * k + r] = key_id(x);
+        a.probs[(size_t)m * k + r] = __expf(key_logit(x) - mu) / S;
+      }
+    }
+    __syncthreads();  // sh is reused by the next row's merge
+    return;
+  } else if (found <= (uint32_t)kCandCap) {
+    block_sort_desc<WAVES>(sh.cand, found);
+    if (tid < k) key = sh.cand[tid];
+  } else {
+    // Massive exact ties: k rounds of "largest key below the previous one"
+    // over the candidate logits.
+    uint64_t prev = ~0ull;
+    for (int r = 0; r < k; ++r) {
+      uint64_t best = 0;
+      for (int e = tid; e < ne; e += NT) {
+        const int j = s_tiles[e / kTileRows] * kTileRows + e % kTileRows;
+        if (j < V) {
+          const float z = zr[j];
+          if (ord_from_f32(z) >= T) {
+            const uint64_t kv = make_key(z, a.t2f[j]);
+            if (kv < prev) best = max_u64(best, kv);
+          }
+        }
+      }
+      best = wave_max_u64(best);
+      __syncthreads();
+      if (tid == 0) sh.kmax = 0;
+      __syncthreads();
+      if (lane == 0) atomicMax(&sh.kmax, (unsigned long long)best);
+      __syncthreads();
+      best = sh.kmax;
+      if (tid == r) key = best;
+      prev = best;
+    }
+  }
+  if (tid < k) {
+    a.full_ids[(size_t)m * k + tid] = key_id(key);
+    a.probs[(size_t)m * k + tid] = __expf(key_logit(key) - mu) / S;
+  }
+  __syncthreads();  // sh is reused by the next row's merge
+}
+
 // ---------------------------------------------------------------- MFMA path
 // Draft trees and batches (M = 3..512 rows): the head is a skinny GEMM, z^T = W_trim h^T.
 // v_mfma_f32_16x16x32_bf16 takes 16 W rows as the A operand and 16 draft rows
@@ -585,6 +743,14 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMfmaWaves = 4;
+// A logit buffer of this size or more is written with streaming stores: left
+// dirty in the L2s it would be written back at the kernel's end, after the
+// last tile, while streaming stores send it to memory during the
+// contraction. Smaller buffers stay in L2 for the merge kernel that reads
+// them back.
+constexpr size_t kZStreamBytes = 6u << 20;
+constexpr int kCpolNt = 2;                     // cache policy: non-temporal (streaming)
+constexpr int kBufferRsrcWord3 = 0x00020000;   // raw 32-bit data, no swizzle
 constexpr int kGroupRows = 64;  // draft rows per MFMA workgroup (4 column blocks)
 
 // W is staged through wave-private LDS: the operand layout (16 rows x 64
@@ -716,6 +882,11 @@ __global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a
   __syncthreads();
   // Top-k mode: the sums go straight to the logit buffer, which the row
   // merge reads; sampling mode keeps them in LDS for the tile epilogue.
+  // Streaming stores go through a buffer resource over the group's rows from
+  // this tile on (uniform base, per-lane byte offsets, bounds-checked).
+  const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
+      a.zbuf + (size_t)mb * a.zpitch + row0, 0,
+      (int)(((size_t)M * a.zpitch - row0) * 4), kBufferRsrcWord3);
   for (int i = threadIdx.x; i < NT * 16 * (kTileRows / 4); i += kMfmaWaves * kWave) {
     const int row = i / (kTileRows / 4), c4 = 4 * (i % (kTileRows / 4));
     f32x4 val = *reinterpret_cast<const f32x4 *>(&sm.part[0][row][c4]);
@@ -728,8 +899,13 @@ __global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a
         if (row0 + c4 + c < a.V_high) val[c] += bf16_to_f32(a.bias[row0 + c4 + c]);
     }
     *reinterpret_cast<f32x4 *>(&sm.part[0][row][c4]) = val;
-    if (!a.sample && row < M)
-      *reinterpret_cast<f32x4 *>(a.zbuf + (size_t)(mb + row) * a.zpitch + row0 + c4) = val;
+    if (!a.sample && row < M) {
+      if (a.zstream)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, val), zrs,
+                                               (row * a.zpitch + c4) * 4, 0, kCpolNt);
+      else
+        *reinterpret_cast<f32x4 *>(a.zbuf + (size_t)(mb + row) * a.zpitch + row0 + c4) = val;
+    }
   }
   __syncthreads();
   if (!a.sample) {
@@ -768,178 +944,26 @@ __global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a
       }
       a.tile_ms[(size_t)(mb + m) * a.tiles + tile] = pack_ms(mu, S);
     }
-    return;
-  }
-
-  const bool valid = row0 + lane < a.V_high;
-  const int32_t fid = valid ? a.t2f[row0 + lane] : 0;
-  // Draft rows in blocks of four: one Philox call per lane and block gives
-  // the variates of all four rows.
-  for (int b = wave; 4 * b < M; b += kMfmaWaves) {
-    const u32x4 x =
-        gumbel_words(a.seed_lo, a.seed_hi, a.off_lo, a.off_hi, mb / 4 + b, row0 + lane);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 4 * b + r;
-      if (m < M)
-        wave_publish_sample(a, mb + m, tile, sm.part[0][m][lane], gumbel_from_word(x[r]),
-                            fid, valid);
-    }
-  }
-}
-
-// Top-k merge of the MFMA path, one workgroup per draft row m, from the
-// tiles' softmax partials and the logits in the workspace:
-//   * the softmax max and sum over the row come from the tile partials,
-//     combined in a fixed order;
-//   * each tile's max is a logit of that tile, so the k-th largest of the
-//     maxima of 64 disjoint groups of tiles (with multiplicity) is at most
-//     the row's k-th largest logit: only tiles whose max reaches it can hold
-//     a pick, typically k to 2k of them;
-//   * the logits of those tiles at or above the bound become keys in LDS
-//     and are ranked as in the tile merge.
-constexpr int kTreeWaves = 8;
-
-template <int WAVES>
-__global__ __launch_bounds__(WAVES *kWave) void tree_merge_kernel(HeadArgs a) {
-  constexpr int NT = WAVES * kWave;
-  constexpr int kTpt = (kMaxTiles + NT - 1) / NT;  // tiles per thread
-  constexpr int GS = NT / kWave;                   // threads per tile group
-  static_assert((GS & (GS - 1)) == 0 && GS <= kWave, "group of threads within a wave");
-  __shared__ MergeShared<WAVES> sh;
-  __shared__ int32_t s_tiles[kMaxTiles];
-  __shared__ uint32_t s_ntiles;
-  const int m = blockIdx.x, tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
-  const int k = a.k, V = a.V_high, tiles = a.tiles;
-  const uint64_t *ms = a.tile_ms + (size_t)m * tiles;
-  const float *zr = a.zbuf + (size_t)m * a.zpitch;
-
-  uint64_t mst[kTpt];
-#pragma unroll
-  for (int j = 0; j < kTpt; ++j) {
-    const int t = tid + j * NT;
-    mst[j] = t < tiles ? ms[t] : 0ull;
-  }
-  float mu_l = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < kTpt; ++j)
-    if (tid + j * NT < tiles) mu_l = fmaxf(mu_l, ms_max(mst[j]));
-  uint32_t gmx = mu_l == -INFINITY ? 0u : ord_from_f32(mu_l);
-#pragma unroll
-  for (int x = 1; x < GS; x <<= 1) gmx = max(gmx, (uint32_t)__shfl_xor((int)gmx, x));
-  if ((lane & (GS - 1)) == 0) sh.gm[tid / GS] = gmx;
-  const float mw = wave_max(mu_l);
-  if (lane == 0) sh.f[wave] = mw;
-  if (tid == 0) {
-    sh.cnt = 0;
-    s_ntiles = 0;
-  }
-  __syncthreads();
-  float mu = sh.f[0];
-  for (int w = 1; w < WAVES; ++w) mu = fmaxf(mu, sh.f[w]);
-  float s_l = 0.f;
-#pragma unroll
-  for (int j = 0; j < kTpt; ++j)
-    if (tid + j * NT < tiles) s_l += ms_sum(mst[j]) * __expf(ms_max(mst[j]) - mu);
-  const float sw = wave_sum(s_l);
-  if (lane == 0) sh.f2[wave] = sw;
-  if (wave == 0) {
-    // k-th largest of the 64 group maxima: count the larger and the
-    // not-smaller ones with broadcast reads of all 64.
-    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-    const uint32_t gv = sh.gm[lane];
-    u32x4v q[kWave / 4];
-#pragma unroll
-    for (int j = 0; j < kWave / 4; ++j) q[j] = *reinterpret_cast<const u32x4v *>(&sh.gm[4 * j]);
-    uint32_t gt = 0, ge = 0;
-#pragma unroll
-    for (int j = 0; j < kWave / 4; ++j)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        gt += q[j][c] > gv;
-        ge += q[j][c] >= gv;
-      }
-    const uint64_t hit = __ballot(gt < (uint32_t)k && ge >= (uint32_t)k);
-    if (lane == 0)
-      sh.T = hit ? (uint32_t)__builtin_amdgcn_readlane((int)gv, __builtin_ctzll(hit)) : 0u;
-  }
-  __syncthreads();
-  const uint32_t T = (uint32_t)sh.T;
-  float S = sh.f2[0];
-  for (int w = 1; w < WAVES; ++w) S += sh.f2[w];
-#pragma unroll
-  for (int j = 0; j < kTpt; ++j) {
-    const int t = tid + j * NT;
-    if (t < tiles && ord_from_f32(ms_max(mst[j])) >= T) s_tiles[atomicAdd(&s_ntiles, 1u)] = t;
-  }
-  __syncthreads();
-  const int ne = (int)s_ntiles * kTileRows;  // candidate logits
-  constexpr int kRound = 4;
-  for (int base = 0; base < ne; base += kRound * NT) {
-    float zv[kRound];
-    int jv[kRound];
-#pragma unroll
-    for (int i = 0; i < kRound; ++i) {
-      const int e = base + i * NT + tid;
-      jv[i] = e < ne ? s_tiles[e / kTileRows] * kTileRows + e % kTileRows : V;
-      zv[i] = jv[i] < V ? zr[jv[i]] : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < kRound; ++i)
-      if (jv[i] < V && ord_from_f32(zv[i]) >= T) {
-        const uint32_t pos = atomicAdd(&sh.cnt, 1u);
-        if (pos < (uint32_t)kCandCap) sh.cand[pos] = make_key(zv[i], a.t2f[jv[i]]);
-      }
-  }
-  __syncthreads();
-  const uint32_t found = sh.cnt;
-  uint64_t key = 0;  // rank `tid` for tid < k
-  if (found <= (uint32_t)kWave) {
-    if (wave == 0) {
-      const uint64_t x = lane < (int)found ? sh.cand[lane] : 0ull;
-      uint32_t r = 0;
-      for (uint32_t j = 0; j < found; ++j) r += sh.cand[j] > x;
-      if (lane < (int)found && r < (uint32_t)k) {
-        a.full_ids[(size_t)m * k + r] = key_id(x);
-        a.probs[(size_t)m * k + r] = __expf(key_logit(x) - mu) / S;
-      }
-    }
-    return;
-  } else if (found <= (uint32_t)kCandCap) {
-    block_sort_desc<WAVES>(sh.cand, found);
-    if (tid < k) key = sh.cand[tid];
   } else {
-    // Massive exact ties: k rounds of "largest key below the previous one"
-    // over the candidate logits.
-    uint64_t prev = ~0ull;
-    for (int r = 0; r < k; ++r) {
-      uint64_t best = 0;
-      for (int e = tid; e < ne; e += NT) {
-        const int j = s_tiles[e / kTileRows] * kTileRows + e % kTileRows;
-        if (j < V) {
-          const float z = zr[j];
-          if (ord_from_f32(z) >= T) {
-            const uint64_t kv = make_key(z, a.t2f[j]);
-            if (kv < prev) best = max_u64(best, kv);
-          }
-        }
+    const bool valid = row0 + lane < a.V_high;
+    const int32_t fid = valid ? a.t2f[row0 + lane] : 0;
+    // Draft rows in blocks of four: one Philox call per lane and block gives
+    // the variates of all four rows.
+    for (int b = wave; 4 * b < M; b += kMfmaWaves) {
+      const u32x4 x =
+          gumbel_words(a.seed_lo, a.seed_hi, a.off_lo, a.off_hi, mb / 4 + b, row0 + lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * b + r;
+        if (m < M)
+          wave_publish_sample(a, mb + m, tile, sm.part[0][m][lane], gumbel_from_word(x[r]),
+                              fid, valid);
       }
-      best = wave_max_u64(best);
-      __syncthreads();
-      if (tid == 0) sh.kmax = 0;
-      __syncthreads();
-      if (lane == 0) atomicMax(&sh.kmax, (unsigned long long)best);
-      __syncthreads();
-      best = sh.kmax;
-      if (tid == r) key = best;
-      prev = best;
     }
   }
-  if (tid < k) {
-    a.full_ids[(size_t)m * k + tid] = key_id(key);
-    a.probs[(size_t)m * k + tid] = __expf(key_logit(key) - mu) / S;
-  }
 }
+
+
 
 // Sampling mode: one workgroup per draft row merges the published tile
 // partials.
@@ -947,6 +971,17 @@ template <int WAVES>
 __global__ __launch_bounds__(WAVES *kWave) void head_merge_kernel(HeadArgs a) {
   __shared__ MergeShared<WAVES> sh;
   sample_merge<WAVES>(a, blockIdx.x, sh);
+}
+
+constexpr int kTreeWaves = 8;
+
+// Top-k mode of the MFMA path: the row merges, one workgroup per draft row.
+template <int WAVES>
+__global__ __launch_bounds__(WAVES *kWave) void tree_merge_kernel(HeadArgs a) {
+  __shared__ MergeShared<WAVES> sh;
+  __shared__ int32_t s_tiles[kMaxTiles];
+  __shared__ uint32_t s_ntiles;
+  row_merge<WAVES>(a, blockIdx.x, sh, s_tiles, s_ntiles);
 }
 
 template <int NT>
@@ -1083,6 +1118,7 @@ hipError_t launch_head_call(const uint16_t *h, int32_t M, int32_t d, const uint1
   a.zbuf = reinterpret_cast<float *>(base + p.off_zbuf);
   a.zpitch = p.tiles * kTileRows;
   a.cgroups = (M + kGroupRows - 1) / kGroupRows;
+  a.zstream = (size_t)M * p.tiles * kTileRows * 4 >= kZStreamBytes ? 1 : 0;
   a.ntt = (M + 15) / 16;
   // Up to kGemvMaxRows rows: one GEMV pass with the merge in the same
   // kernel. More rows: the MFMA skinny GEMM, then one merge workgroup per row.
