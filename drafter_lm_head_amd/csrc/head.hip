@@ -780,7 +780,8 @@ template <int NT>
 constexpr bool kDirectH = NT <= 2;
 
 template <int NT>
-__global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a) {
+__global__ __launch_bounds__(kMfmaWaves *kWave) __attribute__((amdgpu_waves_per_eu(2)))
+void head_mfma_kernel(HeadArgs a) {
   union alignas(16) Smem {
     u32x4 stage[kMfmaWaves][kStageSize];
     float part[kMfmaWaves][NT * 16][kPartPitch];
@@ -803,9 +804,13 @@ __global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a
   const int cq = ((c16 + kMfmaWaves - 1) / kMfmaWaves + 3) / 4 * 4;
   const int c_lo = min(c16, wave * cq), c_hi = min(c16, c_lo + cq);
 
-  // Uniform bases plus 32-bit per-lane offsets (in 16-byte chunks).
-  const u32x4 *tileW = a.W + (size_t)row0 * c16;
-  const int last_row = a.V_high - 1 - row0;  // rows past V_high re-read this one
+  // W loads through a buffer resource over the tile's rows that exist (rows
+  // past V_high read as zero): one per-lane byte offset plus a uniform
+  // offset per group of 4 rows.
+  const int vrows = min(kTileRows, a.V_high - row0);
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u32x4 *>(a.W + (size_t)row0 * c16), 0, vrows * c16 * 16, kBufferRsrcWord3);
+  const int row4_bytes = 4 * c16 * 16;
   u32x4 *st = sm.stage[wave];
 
   f32x4 acc[4][NT];
@@ -815,22 +820,27 @@ __global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a
     for (int cb = 0; cb < NT; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Stage loads: instruction q covers tile rows 4q .. 4q + 3, 256 bytes each.
+  // Every load is issued (chunks past the wave's range re-read its last one
+  // and are zeroed when staged), so the number of loads in flight is fixed.
   auto load_stage = [&](u32x4 (&v)[kStageChunks], int base) {
-    const int ch = base + r16;
+    const int off = (g * c16 + min(base + r16, c_hi - 1)) * 16;
 #pragma unroll
     for (int q = 0; q < kStageChunks; ++q)
-      v[q] = ch < c_hi ? load_stream16(tileW + min(4 * q + g, last_row) * c16 + ch)
-                       : u32x4{0, 0, 0, 0};
+      v[q] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, off, q * row4_bytes, kCpolNt));
   };
-  // One stage: its loads (v) go to LDS, v is refilled with the stage `ahead`
-  // chunks further on, then the B operands of the whole stage (contiguous
-  // loads from L2) and per k-step the A operands from LDS and the MFMAs; the
+  // One stage: its loads (v) go to LDS, then the B operands of the whole
+  // stage are loaded (contiguous loads from L2), then v is refilled with the
+  // next stage, and per k-step the A operands come from LDS for the MFMAs.
+  // The B loads go first so that the MFMAs wait for them only and not for
+  // the next stage, which stays in flight through the stage's MFMAs. The
   // scheduling barriers keep the compiler from hoisting every A read.
-  auto do_stage = [&](u32x4 (&v)[kStageChunks], int base, int ahead) {
+  auto do_stage = [&](u32x4 (&v)[kStageChunks], int base, auto prefetch) {
+    const bool in = base + r16 < c_hi;
 #pragma unroll
-    for (int q = 0; q < kStageChunks; ++q) st[(4 * q + g) * kStagePitch + r16] = v[q];
+    for (int q = 0; q < kStageChunks; ++q)
+      st[(4 * q + g) * kStagePitch + r16] = in ? v[q] : u32x4{0, 0, 0, 0};
     __builtin_amdgcn_wave_barrier();
-    if (base + ahead < c_hi) load_stage(v, base + ahead);
     u32x4 bv[kStageChunks / 4][NT];
 #pragma unroll
     for (int t = 0; t < kStageChunks / 4; ++t) {
@@ -849,6 +859,7 @@ __global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a
           bv[t][cb] = (ok && 4 * cg + cb < a.ntt) ? hs[cb * kWave] : u32x4{0, 0, 0, 0};
       }
     }
+    if constexpr (decltype(prefetch)::value) load_stage(v, base + kStageChunks);
 #pragma unroll
     for (int t = 0; t < kStageChunks / 4; ++t) {
       __builtin_amdgcn_sched_barrier(0);
@@ -866,9 +877,14 @@ __global__ __launch_bounds__(kMfmaWaves *kWave) void head_mfma_kernel(HeadArgs a
     __builtin_amdgcn_wave_barrier();
   };
   u32x4 v[kStageChunks];
-  if (c_lo < c_hi) load_stage(v, c_lo);
+  if (c_lo < c_hi) {
+    load_stage(v, c_lo);
+    int base = c_lo;
 #pragma unroll 1
-  for (int base = c_lo; base < c_hi; base += kStageChunks) do_stage(v, base, kStageChunks);
+    for (; base + kStageChunks < c_hi; base += kStageChunks)
+      do_stage(v, base, std::true_type{});
+    do_stage(v, base, std::false_type{});
+  }
   __syncthreads();  // every wave is done with its stage before part[] reuses it
 
   // Partial products to LDS as [draft row][tile row] (rows padded to break
