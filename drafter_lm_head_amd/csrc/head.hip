@@ -97,7 +97,6 @@ struct alignas(16) MergeShared {
   unsigned long long kmax, T;
   uint32_t cnt;
   float f[WAVES], f2[WAVES], zw[WAVES];
-  uint32_t gm[kWave];                        // group maxima (row merge)
 };
 
 // Ranks (0 = largest) of NR rows of 64 keys in LDS, keys[r * 64 + lane],
@@ -607,7 +606,10 @@ __device__ void row_merge(const HeadArgs &a, int m, MergeShared<WAVES> &sh, int3
   uint32_t gmx = mu_l == -INFINITY ? 0u : ord_from_f32(mu_l);
 #pragma unroll
   for (int x = 1; x < GS; x <<= 1) gmx = max(gmx, (uint32_t)__shfl_xor((int)gmx, x));
-  if ((lane & (GS - 1)) == 0) sh.gm[tid / GS] = gmx;
+  // Group maxima as distinct keys (max, then 64 - group): the key of rank
+  // k - 1 holds the k-th largest maximum counted with multiplicity.
+  if ((lane & (GS - 1)) == 0)
+    sh.sc[0][tid / GS] = ((uint64_t)gmx << 32) | (uint32_t)(kWave - tid / GS);
   const float mw = wave_max(mu_l);
   if (lane == 0) sh.f[wave] = mw;
   if (tid == 0) {
@@ -623,28 +625,23 @@ __device__ void row_merge(const HeadArgs &a, int m, MergeShared<WAVES> &sh, int3
     if (j < tpt && tid + j * NT < tiles) s_l += ms_sum(mst[j]) * __expf(ms_max(mst[j]) - mu);
   const float sw = wave_sum(s_l);
   if (lane == 0) sh.f2[wave] = sw;
-  if (wave == 0) {
-    // k-th largest of the 64 group maxima: count the larger and the
-    // not-smaller ones with broadcast reads of all 64.
-    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-    const uint32_t gv = sh.gm[lane];
-    u32x4v q[kWave / 4];
+  // Rank of each group key: every wave counts the larger keys among its
+  // 64 / WAVES of them (broadcast reads); after the barrier every wave sums
+  // the partial counts and takes the key of rank k - 1.
+  constexpr int kSpan = kWave / WAVES;
+  static_assert(kSpan * WAVES == kWave && WAVES <= 16, "group keys split evenly over the waves");
+  const uint64_t gkey = sh.sc[0][lane];
+  uint32_t c = 0;
 #pragma unroll
-    for (int j = 0; j < kWave / 4; ++j) q[j] = *reinterpret_cast<const u32x4v *>(&sh.gm[4 * j]);
-    uint32_t gt = 0, ge = 0;
-#pragma unroll
-    for (int j = 0; j < kWave / 4; ++j)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        gt += q[j][c] > gv;
-        ge += q[j][c] >= gv;
-      }
-    const uint64_t hit = __ballot(gt < (uint32_t)k && ge >= (uint32_t)k);
-    if (lane == 0)
-      sh.T = hit ? (uint32_t)__builtin_amdgcn_readlane((int)gv, __builtin_ctzll(hit)) : 0u;
-  }
+  for (int j = 0; j < kSpan; ++j) c += sh.sc[0][wave * kSpan + j] > gkey;
+  uint32_t *prank = &sh.prank[0][0][0];
+  prank[wave * kWave + lane] = c;
   __syncthreads();
-  const uint32_t T = (uint32_t)sh.T;
+  uint32_t r = 0;
+#pragma unroll
+  for (int w = 0; w < WAVES; ++w) r += prank[w * kWave + lane];
+  const uint64_t hit = __ballot(r == (uint32_t)(k - 1));
+  const uint32_t T = hit ? (uint32_t)(readlane_u64(gkey, __builtin_ctzll(hit)) >> 32) : 0u;
   float S = sh.f2[0];
   for (int w = 1; w < WAVES; ++w) S += sh.f2[w];
 #pragma unroll
