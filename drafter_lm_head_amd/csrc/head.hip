@@ -94,7 +94,7 @@ struct alignas(16) MergeShared {
   alignas(16) uint64_t cand[kCandCap];       // survivors of the threshold
   alignas(16) uint64_t sc[2][kWave];         // rank inputs / outputs
   uint32_t prank[4][4][kWave];               // partial ranks
-  unsigned long long kmax, T;
+  unsigned long long kmax;
   uint32_t cnt;
   float f[WAVES], f2[WAVES], zw[WAVES];
 };
@@ -316,14 +316,26 @@ __device__ void final_merge(const HeadArgs &a, int m, MergeShared<SW> &sh) {
   __syncthreads();
   float mu = sh.f[0];
   for (int w = 1; w < WAVES; ++w) mu = fmaxf(mu, sh.f[w]);
+  // Rank of each group maximum (distinct keys, 0 for an empty group): every
+  // wave counts the larger keys among its 64 / WAVES of them; after the
+  // barrier every wave sums the partial counts and forms T itself.
+  constexpr int kSpan = kWave / WAVES;
+  static_assert(kSpan * WAVES == kWave && WAVES <= 16, "group keys split evenly over the waves");
+  const uint64_t gkey = sh.sc[0][lane];
+  uint32_t gc = 0;
+#pragma unroll
+  for (int j = 0; j < kSpan; ++j) gc += sh.sc[0][wave * kSpan + j] > gkey;
+  uint32_t *prank = &sh.prank[0][0][0];
+  prank[wave * kWave + lane] = gc;
+  __syncthreads();  // partial ranks ready; all reads of sh.f done
+  uint64_t T;
   {
-    const uint32_t r = block_rank<WAVES, 1>(sh.sc[0], &sh.prank[0][0][0]);
-    if (wave == 0) {
-      const uint64_t hit = __ballot(r == (uint32_t)(k - 1) && g != 0ull);
-      if (lane == 0) sh.T = max_u64(hit ? readlane_u64(g, __builtin_ctzll(hit)) : 0ull, sh.kmax);
-    }
+    uint32_t r = 0;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) r += prank[w * kWave + lane];
+    const uint64_t hit = __ballot(r == (uint32_t)(k - 1) && gkey != 0ull);
+    T = max_u64(hit ? readlane_u64(gkey, __builtin_ctzll(hit)) : 0ull, sh.kmax);
   }
-  __syncthreads();  // all reads of sh.f done, T ready
   if (wave == 0) {  // g and gk are in registers: reset the maxima for the next call
     publish_u64(gmax + lane, 0ull);
     publish_u64(gkth + lane, 0ull);
@@ -334,7 +346,6 @@ __device__ void final_merge(const HeadArgs &a, int m, MergeShared<SW> &sh) {
     if (tid + j * NT < tiles) s_l += ms_sum(mst[j]) * __expf(ms_max(mst[j]) - mu);
   const float s_w = wave_sum(s_l);
   if (lane == 0) sh.f[wave] = s_w;
-  const uint64_t T = sh.T;
 #pragma unroll
   for (int b = 0; b < 2; ++b)
 #pragma unroll
