@@ -44,6 +44,7 @@ struct HeadArgs {
   float *probs;          // [M][k]
   float *logits;         // [M][V_high], logits-only variant
   const u32x4 *hp;       // h in MFMA B-operand order (MFMA path)
+  uint32_t *merged;      // GEMV path, two draft rows: finished row mergers (zero between calls)
   int32_t zstream;       // MFMA path: logits to the workspace with streaming stores
   // Sampling mode (k = 1): the pick is the largest z + Gumbel(seed, offset).
   int32_t sample;
@@ -419,6 +420,36 @@ __device__ void final_merge(const HeadArgs &a, int m, MergeShared<SW> &sh) {
 // would not fit in the registers (long rows with two draft rows) the
 // workgroups have 8 waves and one tile each. Each tile's partial (top-k keys,
 // softmax partial) is published as before.
+// Several draft rows, R = min(rows, workgroups) mergers: the workgroup with
+// the q-th ticket from the end (q = 0: the last to arrive) merges rows q,
+// q + R, ...; all but the last first wait until every workgroup has arrived
+// (a bounded wait: the mergers are resident and no other workgroup waits,
+// so it ends within microseconds). Every thread must call it (it has a
+// barrier).
+constexpr uint32_t kArriveWaitMax = 1u << 20;
+
+__device__ __forceinline__ void wait_arrivals(const uint32_t *counter, uint32_t n) {
+  if (threadIdx.x == 0) {
+    uint32_t spins = 0;
+    while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n &&
+           ++spins < kArriveWaitMax)
+      __builtin_amdgcn_s_sleep(2);
+  }
+  __syncthreads();
+}
+
+// The last of R mergers to finish returns the ticket counter (and the count
+// of finished mergers) to zero: only then has every merger seen the count
+// of arrivals it waited for.
+__device__ __forceinline__ void finish_merge(const HeadArgs &a, int R) {
+  if (threadIdx.x != 0) return;
+  if (R == 1 || __hip_atomic_fetch_add(a.merged, 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)R - 1) {
+    if (R > 1) reset_counter(a.merged);
+    reset_counter(a.counter);
+  }
+}
+
 template <int MT, int CPL>
 constexpr int gemv_waves() {
   return (CPL <= 8 || (MT == 1 && CPL <= 12)) ? 16 : 8;
@@ -532,9 +563,18 @@ __global__ __launch_bounds__(WAVES *kWave) void head_gemv_kernel(HeadArgs a) {
       wave_publish_sample(a, e_m, tile, zl,
                           gumbel(a.seed_lo, a.seed_hi, a.off_lo, a.off_hi, e_m, e_row),
                           fid, valid);
-    if (arrive(a.counter, &s_slot) != gridDim.x - 1) return;
-    for (int m = 0; m < MT; ++m) sample_merge<WAVES>(a, m, sh);
-    if (threadIdx.x == 0) reset_counter(a.counter);
+    const uint32_t ticket = arrive(a.counter, &s_slot);
+    if (MT == 1) {
+      if (ticket != gridDim.x - 1) return;
+      sample_merge<WAVES>(a, 0, sh);
+      if (threadIdx.x == 0) reset_counter(a.counter);
+      return;
+    }
+    const int R = min(MT, (int)gridDim.x), q = (int)gridDim.x - 1 - (int)ticket;
+    if (q >= R) return;
+    if (q > 0) wait_arrivals(a.counter, gridDim.x);
+    for (int m = q; m < MT; m += R) sample_merge<WAVES>(a, m, sh);
+    finish_merge(a, R);
     return;
   }
 
@@ -568,13 +608,23 @@ __global__ __launch_bounds__(WAVES *kWave) void head_gemv_kernel(HeadArgs a) {
     }
   }
 
-  // The last workgroup to finish merges every tile's partial.
-  if (arrive(a.counter, &s_slot) != gridDim.x - 1) return;
-  if (threadIdx.x == 0) reset_counter(a.counter);
+  // The last workgroup to finish merges every tile's partial; with two
+  // draft rows the one before it takes the second row at the same time.
   // The merge is latency-bound: past 8 waves more waves only add work.
+  const uint32_t ticket = arrive(a.counter, &s_slot);
   constexpr int MW = WAVES < 8 ? WAVES : 8;
-  if (wave >= MW) return;
-  for (int m = 0; m < MT; ++m) final_merge<MW, WAVES>(a, m, sh);
+  if (MT == 1) {
+    if (ticket != gridDim.x - 1) return;
+    if (threadIdx.x == 0) reset_counter(a.counter);
+    if (wave >= MW) return;
+    final_merge<MW, WAVES>(a, 0, sh);
+    return;
+  }
+  const int R = min(MT, (int)gridDim.x), q = (int)gridDim.x - 1 - (int)ticket;
+  if (q >= R || wave >= MW) return;
+  if (q > 0) wait_arrivals(a.counter, gridDim.x);
+  for (int m = q; m < MT; m += R) final_merge<MW, WAVES>(a, m, sh);
+  finish_merge(a, R);
 }
 
 // Top-k merge of the MFMA path, one workgroup per draft row m, from the
@@ -1081,8 +1131,9 @@ hipError_t launch_gemv(const HeadArgs &a, hipStream_t stream) {
 static_assert(kDirectH<2> && !kDirectH<3>, "packed h is allocated for more than 32 rows");
 
 HeadPlan head_plan(int32_t M, int32_t V_high, int32_t k) {
-  // Fixed-offset prefix that every call leaves at zero: the ticket counter,
-  // then the group maxima of the GEMV path's draft rows. Per-call data after.
+  // Fixed-offset prefix that every call leaves at zero: the ticket counter
+  // (byte 0), the count of finished row mergers (byte 64), then the group
+  // maxima of the GEMV path's draft rows. Per-call data after.
   HeadPlan p;
   p.tiles = (V_high + kTileRows - 1) / kTileRows;
   size_t off = 256;
@@ -1123,6 +1174,7 @@ hipError_t launch_head_call(const uint16_t *h, int32_t M, int32_t d, const uint1
   a.k = k;
   a.tiles = p.tiles;
   a.counter = reinterpret_cast<uint32_t *>(base);
+  a.merged = reinterpret_cast<uint32_t *>(base + 64);
   a.tile_keys = reinterpret_cast<uint64_t *>(base + p.off_tile_keys);
   a.tile_ms = reinterpret_cast<uint64_t *>(base + p.off_tile_ms);
   a.group_max = reinterpret_cast<uint64_t *>(base + p.off_group);
