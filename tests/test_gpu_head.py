@@ -110,12 +110,14 @@ def test_large_vocab_tail_rows(dlh, V_high, d, M):
     check_case(dlh, h, W, t2f, 10)
 
 
-def test_large_vocab_repeatable(dlh):
+@pytest.mark.parametrize("M", [1, 2])
+def test_large_vocab_repeatable(dlh, M):
     # Which wave computes a row changes from call to call (rows are taken
-    # from a counter); the results must not.
-    h, W, t2f = rand_case(77, 1, 4096, 32768)
+    # from a counter), and with two rows which workgroups merge them; the
+    # results must not, and the counters must be back at zero.
+    h, W, t2f = rand_case(77, M, 4096, 32768)
     hd, Wd, td = to_dev_bf16(h), to_dev_bf16(W), to_dev_i32(t2f)
-    n = dlh.vt_draft_head_workspace_size(1, 32768, 4096, 10)
+    n = dlh.vt_draft_head_workspace_size(M, 32768, 4096, 10)
     ws = torch.zeros(n, dtype=torch.uint8, device=DEV)
     ref = None
     for _ in range(30):
@@ -125,6 +127,14 @@ def test_large_vocab_repeatable(dlh):
         assert cur == ref
     torch.cuda.synchronize()
     assert int(ws[:256 + 2 * 2 * 64 * 8].to(torch.int64).sum().item()) == 0
+
+
+@pytest.mark.parametrize("V_high", [1, 37, 64, 65, 128, 200])
+def test_two_rows_few_workgroups(dlh, V_high):
+    # One workgroup merges both rows; from two workgroups on the last two
+    # merge one row each.
+    h, W, t2f = rand_case(300 + V_high, 2, 512, V_high, hscale=3.0)
+    check_case(dlh, h, W, t2f, min(10, V_high))
 
 
 @pytest.mark.parametrize("k", [1, 2, 31, 32, 63, 64])

@@ -56,6 +56,21 @@ def test_draws_match_oracle_gemv_and_mfma(dlh, M):
         assert check_draws(ids, probs, h, W, t2f, 0xDEADBEEF12345, off) <= max(1, M // 64)
 
 
+@pytest.mark.parametrize("V_high", [1, 64, 65, 200, 40000])
+def test_two_row_draws_few_and_many_workgroups(dlh, V_high):
+    # Two rows: one merging workgroup (one tile) or two in parallel; the
+    # counters must be back at zero after every call.
+    h, W, t2f = rand_case(700 + V_high, 2, 256, V_high, hscale=4.0)
+    hd, Wd, td = to_dev_bf16(h), to_dev_bf16(W), to_dev_i32(t2f)
+    ws = torch.zeros(dlh.vt_draft_head_workspace_size(2, V_high, 256, 1), dtype=torch.uint8,
+                     device=DEV)
+    for off in (0, 1, 2):
+        ids, probs = dlh.vt_draft_sample(hd, Wd, td, 99, off, ws=ws)
+        torch.cuda.synchronize()
+        assert check_draws(ids.cpu().numpy(), probs.cpu().numpy(), h, W, t2f, 99, off) <= 1
+        assert int(ws[:256].to(torch.int64).sum().item()) == 0
+
+
 def test_draws_are_reproducible_and_move_with_offset(dlh):
     h, W, t2f = rand_case(5, 4, 256, 2048, hscale=2.0)
     a = draw(dlh, h, W, t2f, 1, 10)
