@@ -28,7 +28,7 @@ __device__ __forceinline__ void count_one(int32_t id, uint32_t lo, uint32_t nb,
 
 __global__ __launch_bounds__(kCountThreads) void count_partial_kernel(
     const int32_t *__restrict__ ids, uint64_t n, int32_t V, int32_t range_bins,
-    int32_t n_ranges, int32_t n_chunks, uint64_t chunk_len,
+    int32_t n_ranges, int32_t n_chunks, uint64_t chunk_len, int32_t pitch,
     uint32_t *__restrict__ partial, unsigned long long *__restrict__ inv_part) {
   extern __shared__ uint32_t s_bins[];
   __shared__ unsigned long long s_inv;
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kCountThreads) void count_partial_kernel(
   if (tally && inv) atomicAdd(&s_inv, inv);
   __syncthreads();
 
-  uint32_t *row = partial + (size_t)c * (size_t)V + lo;
+  uint32_t *row = partial + (size_t)c * (size_t)pitch + lo;
   for (uint32_t i = threadIdx.x; i < nb; i += kCountThreads) row[i] = s_bins[i];
   if (tally && threadIdx.x == 0) inv_part[c] = s_inv;
 }
@@ -112,6 +112,30 @@ __device__ __forceinline__ void count_one16(int32_t id, uint32_t lo, uint32_t nb
     const uint32_t sh = (b & 1u) << 4;
     const uint32_t old = atomicAdd(&s_words[b >> 1], 1u << sh);
     if (((old >> sh) & 0xFFFFu) == 0x7FFFu) {
+      atomicSub(&s_words[b >> 1], 0x8000u << sh);
+      const uint32_t pos = atomicAdd(s_nspill, 1u);
+      if (pos < (uint32_t)kSpillCap) s_spill[pos] = lo + b;
+    }
+  }
+}
+
+// The same for N ids at once: every atomic of the batch is issued before
+// any returned value is looked at, so that a wave waits for the LDS once per
+// batch rather than once per id.
+template <int N>
+__device__ __forceinline__ void count_batch16(const int32_t (&id)[N], uint32_t lo, uint32_t nb,
+                                              uint32_t *s_words, uint32_t *s_spill,
+                                              uint32_t *s_nspill) {
+  uint32_t old[N];
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    const uint32_t b = (uint32_t)id[e] - lo;
+    old[e] = b < nb ? atomicAdd(&s_words[b >> 1], 1u << ((b & 1u) << 4)) : 0u;
+  }
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    const uint32_t b = (uint32_t)id[e] - lo, sh = (b & 1u) << 4;
+    if (b < nb && ((old[e] >> sh) & 0xFFFFu) == 0x7FFFu) {
       atomicSub(&s_words[b >> 1], 0x8000u << sh);
       const uint32_t pos = atomicAdd(s_nspill, 1u);
       if (pos < (uint32_t)kSpillCap) s_spill[pos] = lo + b;
@@ -159,15 +183,18 @@ __global__ __launch_bounds__(kCountThreads) void count_partial16_kernel(
       u32x4 q[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) q[u] = load_stream16(v4 + i + u * kCountThreads);
+      int32_t a[4 * kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        const int32_t a[4] = {(int32_t)q[u].x, (int32_t)q[u].y, (int32_t)q[u].z,
-                              (int32_t)q[u].w};
+        a[4 * u] = (int32_t)q[u].x;
+        a[4 * u + 1] = (int32_t)q[u].y;
+        a[4 * u + 2] = (int32_t)q[u].z;
+        a[4 * u + 3] = (int32_t)q[u].w;
+      }
+      count_batch16(a, lo, nb, s_words, s_spill, &s_nspill);
+      if (tally) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          count_one16(a[e], lo, nb, s_words, s_spill, &s_nspill);
-          if (tally) inv += (uint32_t)a[e] >= (uint32_t)V;
-        }
+        for (int e = 0; e < 4 * kUnroll; ++e) inv += (uint32_t)a[e] >= (uint32_t)V;
       }
     }
     for (; i < n4; i += kCountThreads) {
@@ -210,22 +237,42 @@ __device__ __forceinline__ void reduce_invalid(const unsigned long long *__restr
   }
 }
 
-// Sums of the 16-bit partial rows, two ids per thread.
-__global__ __launch_bounds__(256) void count_reduce16_kernel(
+// Sums of the 16-bit partial rows. A workgroup takes 512 ids, 8 per lane
+// (one 16-byte load per row; the row pitch is a multiple of 8 ids, so a
+// load never leaves its row); its 8 waves split the rows, and the 8
+// partial sums are added in LDS in a fixed order.
+constexpr int kRedWaves = 8;
+constexpr int kRedIds = 8 * kWave;  // ids per workgroup
+
+__global__ __launch_bounds__(kRedWaves *kWave) void count_reduce16_kernel(
     const uint16_t *__restrict__ partial, const unsigned long long *__restrict__ inv_part,
     int32_t V, int32_t pitch, int32_t n_chunks, int accumulate, uint32_t *__restrict__ counts,
     uint64_t *__restrict__ n_invalid) {
-  const int32_t v = 2 * (blockIdx.x * 256 + threadIdx.x);
-  if (v < V) {
-    uint32_t s0 = 0, s1 = 0;
-    for (int c = 0; c < n_chunks; ++c) {
-      const uint32_t w =
-          reinterpret_cast<const uint32_t *>(partial + (size_t)c * (size_t)pitch)[v / 2];
-      s0 += w & 0xFFFFu;
-      s1 += w >> 16;
+  __shared__ u32x4 s_sum[kRedWaves][2 * kWave];
+  const int lane = __lane_id(), wave = threadIdx.x / kWave;
+  const int32_t v0 = blockIdx.x * kRedIds + 8 * lane;
+  uint32_t s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (v0 < V) {
+#pragma unroll 8
+    for (int c = wave; c < n_chunks; c += kRedWaves) {
+      const u32x4 w = *reinterpret_cast<const u32x4 *>(partial + (size_t)c * (size_t)pitch + v0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s[2 * j] += w[j] & 0xFFFFu;
+        s[2 * j + 1] += w[j] >> 16;
+      }
     }
-    counts[v] = (accumulate ? counts[v] : 0u) + s0;
-    if (v + 1 < V) counts[v + 1] = (accumulate ? counts[v + 1] : 0u) + s1;
+  }
+  s_sum[wave][2 * lane] = u32x4{s[0], s[1], s[2], s[3]};
+  s_sum[wave][2 * lane + 1] = u32x4{s[4], s[5], s[6], s[7]};
+  __syncthreads();
+  const int32_t v = blockIdx.x * kRedIds + threadIdx.x;
+  if (v < V) {
+    uint32_t tot = accumulate ? counts[v] : 0u;
+#pragma unroll
+    for (int w = 0; w < kRedWaves; ++w)
+      tot += reinterpret_cast<const uint32_t *>(s_sum[w])[threadIdx.x];
+    counts[v] = tot;
   }
   reduce_invalid(inv_part, n_chunks, accumulate, n_invalid);
 }
@@ -238,15 +285,33 @@ __global__ __launch_bounds__(256) void count_spill_kernel(const uint32_t *__rest
   for (uint32_t i = threadIdx.x; i < ns; i += 256) atomicAdd(&counts[sp[1 + i]], 32768u);
 }
 
-__global__ __launch_bounds__(256) void count_reduce_kernel(
+// Sums of the 32-bit partial rows, laid out as the 16-bit reduction: 4 ids
+// per lane (the row pitch is a multiple of 4 ids), rows split over the
+// waves, partial sums added in LDS in a fixed order.
+__global__ __launch_bounds__(kRedWaves *kWave) void count_reduce_kernel(
     const uint32_t *__restrict__ partial, const unsigned long long *__restrict__ inv_part,
-    int32_t V, int32_t n_chunks, int accumulate, uint32_t *__restrict__ counts,
+    int32_t V, int32_t pitch, int32_t n_chunks, int accumulate, uint32_t *__restrict__ counts,
     uint64_t *__restrict__ n_invalid) {
-  const int32_t v = blockIdx.x * 256 + threadIdx.x;
-  if (v < V) {
-    uint32_t s = accumulate ? counts[v] : 0u;
-    for (int c = 0; c < n_chunks; ++c) s += partial[(size_t)c * V + v];
-    counts[v] = s;
+  __shared__ u32x4 s_sum[kRedWaves][kWave];
+  const int lane = __lane_id(), wave = threadIdx.x / kWave;
+  const int32_t v0 = blockIdx.x * (4 * kWave) + 4 * lane;
+  u32x4 s = {0, 0, 0, 0};
+  if (v0 < V) {
+#pragma unroll 8
+    for (int c = wave; c < n_chunks; c += kRedWaves)
+      s += *reinterpret_cast<const u32x4 *>(partial + (size_t)c * (size_t)pitch + v0);
+  }
+  s_sum[wave][lane] = s;
+  __syncthreads();
+  if (threadIdx.x < 4 * kWave) {
+    const int32_t v = blockIdx.x * (4 * kWave) + threadIdx.x;
+    if (v < V) {
+      uint32_t tot = accumulate ? counts[v] : 0u;
+#pragma unroll
+      for (int w = 0; w < kRedWaves; ++w)
+        tot += reinterpret_cast<const uint32_t *>(s_sum[w])[threadIdx.x];
+      counts[v] = tot;
+    }
   }
   reduce_invalid(inv_part, n_chunks, accumulate, n_invalid);
 }
@@ -261,12 +326,11 @@ CountPlan count_plan(uint64_t n, int32_t V) {
   p.range_bins = (V + p.n_ranges - 1) / p.n_ranges;
   if (p.bins16) p.range_bins = (p.range_bins + 1) / 2 * 2;  // word-aligned ranges
   // Chunks of ids: a multiple of 8 (whole chunks per XCD), at least 64k ids
-  // each. 32-bit bins: at most kMaxChunks (with 4 ranges, 256 workgroups,
-  // one per CU). 16-bit bins: about 256 workgroups over the ranges, and
-  // enough chunks that no workgroup sees more than kSpillCap * 32768 ids
-  // (the bound on its overflow records).
+  // each, and about 256 workgroups over the ranges (one per CU). 16-bit
+  // bins: also enough chunks that no workgroup sees more than
+  // kSpillCap * 32768 ids (the bound on its overflow records).
   int64_t c = (int64_t)((n + 65535) / 65536);
-  const int64_t cap = p.bins16 ? (256 / p.n_ranges + 7) / 8 * 8 : kMaxChunks;
+  const int64_t cap = (kMaxChunks / p.n_ranges + 7) / 8 * 8;
   if (c > cap) c = cap;
   if (p.bins16) {
     const uint64_t per = (uint64_t)kSpillCap << 15;
@@ -278,7 +342,7 @@ CountPlan count_plan(uint64_t n, int32_t V) {
   uint64_t len = (n + c - 1) / c;
   p.chunk_len = (len + 3) / 4 * 4;
   if (p.chunk_len == 0) p.chunk_len = 4;
-  p.row_pitch = p.bins16 ? (V + 7) / 8 * 8 : V;
+  p.row_pitch = p.bins16 ? (V + 7) / 8 * 8 : (V + 3) / 4 * 4;
   p.partial_bytes =
       align_up((size_t)p.n_chunks * (size_t)p.row_pitch * (p.bins16 ? 2 : 4), 256);
   p.inv_bytes = align_up((size_t)p.n_chunks * 8, 256);
@@ -316,7 +380,8 @@ hipError_t launch_count(const int32_t *ids, uint64_t n, int32_t V,
                        p.row_pitch, partial, inv, spill);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(count_reduce16_kernel, dim3((V + 511) / 512), dim3(256), 0, stream,
+    hipLaunchKernelGGL(count_reduce16_kernel, dim3((V + kRedIds - 1) / kRedIds),
+                       dim3(kRedWaves * kWave), 0, stream,
                        partial, inv, V, p.row_pitch, p.n_chunks, accumulate, counts, n_invalid);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -328,12 +393,12 @@ hipError_t launch_count(const int32_t *ids, uint64_t n, int32_t V,
   const size_t lds = (size_t)p.range_bins * 4;
   hipLaunchKernelGGL(count_partial_kernel, dim3(slots * 8), dim3(kCountThreads),
                      lds, stream, ids, n, V, p.range_bins, p.n_ranges,
-                     p.n_chunks, p.chunk_len, partial, inv);
+                     p.n_chunks, p.chunk_len, p.row_pitch, partial, inv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(count_reduce_kernel, dim3((V + 255) / 256), dim3(256), 0,
-                     stream, partial, inv, V, p.n_chunks, accumulate, counts,
-                     n_invalid);
+  hipLaunchKernelGGL(count_reduce_kernel, dim3((V + 4 * kWave - 1) / (4 * kWave)),
+                     dim3(kRedWaves * kWave), 0, stream, partial, inv, V, p.row_pitch,
+                     p.n_chunks, accumulate, counts, n_invalid);
   return hipGetLastError();
 }
 

@@ -16,7 +16,7 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 constexpr int kRangeBinsMax = 38912;  // 152 KB
 constexpr int kRange16Max = 76800;    // 16-bit bins: 150 KB
 constexpr int kSpillCap = 1024;       // overflow records per 16-bit workgroup
-constexpr int kMaxChunks = 64;        // rows of the partial histogram table
+constexpr int kMaxChunks = 256;       // counting workgroups (chunks x ranges), about one per CU
 
 struct CountPlan {
   int32_t n_ranges, range_bins, n_chunks;
