@@ -837,7 +837,12 @@ __global__ __launch_bounds__(kWave) void h_pack_kernel(const u32x4 *__restrict__
 template <int NT>
 constexpr bool kDirectH = NT <= 2;
 
-template <int NT>
+// kShared: more than one group of draft rows, so every W tile is read by
+// several workgroups of one XCD. W is then loaded with the plain cache
+// policy and the tile stays in L2 for the other groups (non-temporal loads
+// sent them to HBM: M = 512 294 -> 227 us, M = 128 98 -> 83 us); a tile read
+// once streams past the caches (plain loads cost 4.5 us at M = 60).
+template <int NT, bool kShared>
 __global__ __launch_bounds__(kMfmaWaves *kWave) __attribute__((amdgpu_waves_per_eu(2)))
 void head_mfma_kernel(HeadArgs a) {
   union alignas(16) Smem {
@@ -885,7 +890,8 @@ void head_mfma_kernel(HeadArgs a) {
 #pragma unroll
     for (int q = 0; q < kStageChunks; ++q)
       v[q] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, off, q * row4_bytes, kCpolNt));
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, off, q * row4_bytes,
+                                                       kShared ? 0 : kCpolNt));
   };
   // One stage: its loads (v) go to LDS, then the B operands of the whole
   // stage are loaded (contiguous loads from L2), then v is refilled with the
@@ -1068,8 +1074,12 @@ hipError_t launch_mfma(const HeadArgs &a, hipStream_t stream) {
     if (e0 != hipSuccess) return e0;
   }
   const int slots = (a.tiles + 7) / 8 * a.cgroups;  // per XCD
-  hipLaunchKernelGGL((head_mfma_kernel<NT>), dim3(8 * slots), dim3(kMfmaWaves * kWave), 0,
-                     stream, a);
+  if (NT == 4 && a.cgroups > 1)
+    hipLaunchKernelGGL((head_mfma_kernel<4, true>), dim3(8 * slots), dim3(kMfmaWaves * kWave),
+                       0, stream, a);
+  else
+    hipLaunchKernelGGL((head_mfma_kernel<NT, false>), dim3(8 * slots),
+                       dim3(kMfmaWaves * kWave), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.sample)
