@@ -1064,6 +1064,187 @@ __global__ __launch_bounds__(WAVES *kWave) void tree_merge_kernel(HeadArgs a) {
   row_merge<WAVES>(a, blockIdx.x, sh, s_tiles, s_ntiles);
 }
 
+// ------------------------------------------- MFMA path, many draft rows
+// Past 64 draft rows (top-k mode) the contraction is tiled as a GEMM: a
+// workgroup of 4 waves computes 128 W rows (two tiles) x 128 draft rows (two
+// groups of 64). Per K step of 64 both operand tiles (128 rows x 128 bytes
+// each, W from W_trim, the B operand straight from h) are staged in LDS,
+// double buffered with one barrier per step, and wave (wr, wc) owns the
+// 64 x 64 block of tile 2 p + wr and row group 2 q + wc over the whole of d,
+// so it ends with final sums: logits and the (draft row, tile) softmax
+// partials go out as on the 64-row path and the same row merge follows.
+// Against one 64 x 64 block per workgroup this halves the L2 traffic per
+// flop, which bounds the contraction at these sizes.
+constexpr int kGemmRows = 128;               // W rows and draft rows per workgroup
+constexpr int kGemmKC = 8;                   // 16-byte chunks per row and K step
+constexpr int kGemmPitch = kGemmKC + 1;      // staged row pitch in chunks
+constexpr int kGemmThreads = 4 * kWave;
+
+struct GemmStage {
+  u32x4 w[kGemmRows * kGemmPitch];
+  u32x4 h[kGemmRows * kGemmPitch];
+};
+
+// kShared: more than one pair of row groups, so each pair of W tiles is read
+// by several workgroups of one XCD (plain loads keep it in L2 for them).
+template <bool kShared>
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void head_gemm_kernel(HeadArgs a) {
+  __shared__ GemmStage sm[2];
+  const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
+  const int tpairs = (a.tiles + 1) / 2, gpairs = (a.M + kGemmRows - 1) / kGemmRows;
+  // Workgroup -> (tile pair p, row-group pair q): the pairs q of one p take
+  // consecutive slots of one XCD, so that the W rows come from HBM once.
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int q = slot % gpairs, p = xcd + 8 * (slot / gpairs);
+  if (p >= tpairs) return;
+  const int c16 = a.c16;
+  const int wrow0 = p * kGemmRows, mrow0 = q * kGemmRows;
+  // Buffer resources over the rows that exist: W rows past V_high and draft
+  // rows past M read as zero.
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u32x4 *>(a.W + (size_t)wrow0 * c16), 0,
+      min(kGemmRows, a.V_high - wrow0) * c16 * 16, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t hres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u32x4 *>(a.h + (size_t)mrow0 * c16), 0,
+      min(kGemmRows, a.M - mrow0) * c16 * 16, kBufferRsrcWord3);
+  // Thread tid stages chunk tid % 8 of rows tid / 8 + 32 j, j = 0..3, of
+  // both operands (8 lanes read one row's 128 bytes).
+  const int lr = tid >> 3, lc = tid & 7;
+  const int steps = (c16 + kGemmKC - 1) / kGemmKC;
+  // Two steps in flight: register sets x (even steps) and y (odd steps).
+  // Every load is issued (a step past the last re-reads the last one), so
+  // the number of loads in flight is fixed and each wait covers one set.
+  u32x4 xw[4], xh[4], yw[4], yh[4];
+  auto load = [&](u32x4 (&vw)[4], u32x4 (&vh)[4], int s) {
+    // chunks past d are zeroed when staged
+    const int ch = min(min(s, steps - 1) * kGemmKC + lc, c16 - 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int off = ((lr + 32 * j) * c16 + ch) * 16;
+      vw[j] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, off, 0, kShared ? 0 : kCpolNt));
+      vh[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hres, off, 0, 0));
+    }
+  };
+  const int wr = wave >> 1, wc = wave & 1;
+  const int g = lane >> 4, r16 = lane & 15;
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // One step: its registers go to LDS buffer s % 2, then (after the
+  // barrier) the same registers are refilled with step s + 2 and the MFMAs
+  // run on the buffer.
+  auto do_step = [&](u32x4 (&vw)[4], u32x4 (&vh)[4], int s) {
+    GemmStage &st = sm[s & 1];
+    const bool in = s * kGemmKC + lc < c16;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      st.w[(lr + 32 * j) * kGemmPitch + lc] = in ? vw[j] : u32x4{0, 0, 0, 0};
+      st.h[(lr + 32 * j) * kGemmPitch + lc] = in ? vh[j] : u32x4{0, 0, 0, 0};
+    }
+    // The stage is complete, and every wave is done with the buffer the
+    // next stage overwrites (it read it two stages ago).
+    __syncthreads();
+    // The scheduling barriers keep every set's loads in issue order (set x
+    // before set y), which lets each wait cover one set only.
+    __builtin_amdgcn_sched_barrier(0);
+    load(vw, vh, s + 2);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < kGemmKC / 4; ++t) {
+      const int cl = 4 * t + g;
+      u32x4 av[4], bv[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) av[rb] = st.w[(64 * wr + 16 * rb + r16) * kGemmPitch + cl];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) bv[cb] = st.h[(64 * wc + 16 * cb + r16) * kGemmPitch + cl];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, av[rb]), __builtin_bit_cast(bf16x8, bv[cb]),
+              acc[rb][cb], 0, 0, 0);
+    }
+  };
+  load(xw, xh, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load(yw, yh, 1);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll 1
+  for (int s = 0; s < steps; s += 2) {
+    do_step(xw, xh, s);
+    do_step(yw, yh, s + 1);  // past the last step: every chunk is zeroed
+  }
+
+  // Epilogue of wave (wr, wc): lane (g, r16) holds, per (rb, cb), the
+  // logits of tile rows 16 rb + 4 g .. + 3 for draft row 16 cb + r16.
+  const int tile = 2 * p + wr;
+  if (tile >= a.tiles) return;
+  const int trow0 = tile * kTileRows;
+  const int mw0 = mrow0 + 64 * wc;  // the wave's first draft row
+  // Over the wave's draft rows that exist, from this tile on (none: no
+  // stores follow).
+  const int zrows = min(64, a.M - mw0);
+  const __amdgpu_buffer_rsrc_t zres = __builtin_amdgcn_make_buffer_rsrc(
+      a.zbuf + (size_t)max(0, min(mw0, a.M - 1)) * a.zpitch + trow0, 0,
+      zrows > 0 ? (int)(((size_t)zrows * a.zpitch - trow0) * 4) : 0, kBufferRsrcWord3);
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const int m = mw0 + 16 * cb + r16;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = trow0 + 16 * rb + 4 * g + i;
+        if (a.bias && row < a.V_high) acc[rb][cb][i] += bf16_to_f32(a.bias[row]);
+        if (row < a.V_high) mx = fmaxf(mx, acc[rb][cb][i]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    float S = 0.f;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (trow0 + 16 * rb + 4 * g + i < a.V_high) S += __expf(acc[rb][cb][i] - mx);
+    S += __shfl_xor(S, 16);
+    S += __shfl_xor(S, 32);
+    if (m < a.M) {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const int off = ((16 * cb + r16) * a.zpitch + 16 * rb + 4 * g) * 4;
+        if (a.zstream)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[rb][cb]), zres,
+                                                 off, 0, kCpolNt);
+        else
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[rb][cb]), zres,
+                                                 off, 0, 0);
+      }
+      if (g == 0) a.tile_ms[(size_t)m * a.tiles + tile] = pack_ms(mx, S);
+    }
+  }
+}
+
+hipError_t launch_gemm(const HeadArgs &a, hipStream_t stream) {
+  const int tpairs = (a.tiles + 1) / 2, gpairs = (a.M + kGemmRows - 1) / kGemmRows;
+  const dim3 grid(8 * ((tpairs + 7) / 8) * gpairs), block(kGemmThreads);
+  if (gpairs > 1)
+    hipLaunchKernelGGL((head_gemm_kernel<true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((head_gemm_kernel<false>), grid, block, 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((tree_merge_kernel<kTreeWaves>), dim3(a.M), dim3(kTreeWaves * kWave), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
 template <int NT>
 hipError_t launch_mfma(const HeadArgs &a, hipStream_t stream) {
   const int steps = (a.c16 + 3) / 4;
@@ -1209,6 +1390,7 @@ hipError_t launch_head_call(const uint16_t *h, int32_t M, int32_t d, const uint1
   // Up to kGemvMaxRows rows: one GEMV pass with the merge in the same
   // kernel. More rows: the MFMA skinny GEMM, then one merge workgroup per row.
   if (M <= kGemvMaxRows) return launch_gemv(a, stream);
+  if (M > kGroupRows && !sample) return launch_gemm(a, stream);
   switch ((M + 15) / 16) {
     case 1: return launch_mfma<1>(a, stream);
     case 2: return launch_mfma<2>(a, stream);
