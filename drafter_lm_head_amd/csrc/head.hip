@@ -1065,14 +1065,15 @@ __global__ __launch_bounds__(WAVES *kWave) void tree_merge_kernel(HeadArgs a) {
 }
 
 // ------------------------------------------- MFMA path, many draft rows
-// Past 64 draft rows (top-k mode) the contraction is tiled as a GEMM: a
+// Past 64 draft rows the contraction is tiled as a GEMM: a
 // workgroup of 4 waves computes 128 W rows (two tiles) x 128 draft rows (two
 // groups of 64). Per K step of 64 both operand tiles (128 rows x 128 bytes
 // each, W from W_trim, the B operand straight from h) are staged in LDS,
 // double buffered with one barrier per step, and wave (wr, wc) owns the
 // 64 x 64 block of tile 2 p + wr and row group 2 q + wc over the whole of d,
 // so it ends with final sums: logits and the (draft row, tile) softmax
-// partials go out as on the 64-row path and the same row merge follows.
+// partials (or the tile's draws) go out as on the 64-row path and the same
+// row merges follow.
 // Against one 64 x 64 block per workgroup this halves the L2 traffic per
 // flop, which bounds the contraction at these sizes.
 constexpr int kGemmRows = 128;               // W rows and draft rows per workgroup
@@ -1184,9 +1185,50 @@ void head_gemm_kernel(HeadArgs a) {
   // Epilogue of wave (wr, wc): lane (g, r16) holds, per (rb, cb), the
   // logits of tile rows 16 rb + 4 g .. + 3 for draft row 16 cb + r16.
   const int tile = 2 * p + wr;
-  if (tile >= a.tiles) return;
   const int trow0 = tile * kTileRows;
   const int mw0 = mrow0 + 64 * wc;  // the wave's first draft row
+  if (a.sample) {
+    // Sampling: the wave's block goes to LDS as [draft row][tile row] (the
+    // stage buffers are free once every wave is past its last step), then
+    // the draw runs per tile row as on the 64-row path: one Philox call per
+    // lane and block of four draft rows gives the variates of all four.
+    __syncthreads();
+    if (tile >= a.tiles) return;
+    float *zs = reinterpret_cast<float *>(&sm[0]) + wave * (kWave * kPartPitch);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        f32x4 v = acc[rb][cb];
+        if (a.bias) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = trow0 + 16 * rb + 4 * g + i;
+            if (row < a.V_high) v[i] += bf16_to_f32(a.bias[row]);
+          }
+        }
+        *reinterpret_cast<f32x4 *>(zs + (16 * cb + r16) * kPartPitch + 16 * rb + 4 * g) = v;
+      }
+    // The wave reads what its own lanes wrote: keep the compiler from
+    // moving the reads up, and let the writes land first.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    const bool valid = trow0 + lane < a.V_high;
+    const int32_t fid = valid ? a.t2f[trow0 + lane] : 0;
+    for (int b = 0; b < kWave / 4 && mw0 + 4 * b < a.M; ++b) {
+      const u32x4 x =
+          gumbel_words(a.seed_lo, a.seed_hi, a.off_lo, a.off_hi, mw0 / 4 + b, trow0 + lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = mw0 + 4 * b + r;
+        if (m < a.M)
+          wave_publish_sample(a, m, tile, zs[(4 * b + r) * kPartPitch + lane],
+                              gumbel_from_word(x[r]), fid, valid);
+      }
+    }
+    return;
+  }
+  if (tile >= a.tiles) return;
   // Over the wave's draft rows that exist, from this tile on (none: no
   // stores follow).
   const int zrows = min(64, a.M - mw0);
@@ -1240,8 +1282,11 @@ hipError_t launch_gemm(const HeadArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((head_gemm_kernel<false>), grid, block, 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((tree_merge_kernel<kTreeWaves>), dim3(a.M), dim3(kTreeWaves * kWave), 0,
-                     stream, a);
+  if (a.sample)
+    hipLaunchKernelGGL((head_merge_kernel<8>), dim3(a.M), dim3(8 * kWave), 0, stream, a);
+  else
+    hipLaunchKernelGGL((tree_merge_kernel<kTreeWaves>), dim3(a.M), dim3(kTreeWaves * kWave), 0,
+                       stream, a);
   return hipGetLastError();
 }
 
@@ -1390,7 +1435,7 @@ hipError_t launch_head_call(const uint16_t *h, int32_t M, int32_t d, const uint1
   // Up to kGemvMaxRows rows: one GEMV pass with the merge in the same
   // kernel. More rows: the MFMA skinny GEMM, then one merge workgroup per row.
   if (M <= kGemvMaxRows) return launch_gemv(a, stream);
-  if (M > kGroupRows && !sample) return launch_gemm(a, stream);
+  if (M > kGroupRows) return launch_gemm(a, stream);
   switch ((M + 15) / 16) {
     case 1: return launch_mfma<1>(a, stream);
     case 2: return launch_mfma<2>(a, stream);
