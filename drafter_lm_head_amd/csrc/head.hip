@@ -51,7 +51,6 @@ struct HeadArgs {
   uint32_t seed_lo, seed_hi, off_lo, off_hi;
   uint64_t *tile_z;      // [M][tiles]: bits of z of each tile's drawn row
   const uint16_t *bias;  // bf16[V_high] added to every logit, or nullptr
-  int32_t cgroups;       // MFMA path: groups of kGroupRows draft rows
   int32_t ntt;           // MFMA path: 16-row column blocks over all M rows
   float *zbuf;           // MFMA path, top-k mode: logits [M][zpitch]
   int32_t zpitch;        // tiles * kTileRows floats
@@ -837,12 +836,10 @@ __global__ __launch_bounds__(kWave) void h_pack_kernel(const u32x4 *__restrict__
 template <int NT>
 constexpr bool kDirectH = NT <= 2;
 
-// kShared: more than one group of draft rows, so every W tile is read by
-// several workgroups of one XCD. W is then loaded with the plain cache
-// policy and the tile stays in L2 for the other groups (non-temporal loads
-// sent them to HBM: M = 512 294 -> 227 us, M = 128 98 -> 83 us); a tile read
-// once streams past the caches (plain loads cost 4.5 us at M = 60).
-template <int NT, bool kShared>
+// Up to 64 draft rows, one workgroup per tile; each W tile is read once and
+// streams past the caches (non-temporal loads; plain ones cost 4.5 us at
+// M = 60).
+template <int NT>
 __global__ __launch_bounds__(kMfmaWaves *kWave) __attribute__((amdgpu_waves_per_eu(2)))
 void head_mfma_kernel(HeadArgs a) {
   union alignas(16) Smem {
@@ -851,16 +848,9 @@ void head_mfma_kernel(HeadArgs a) {
   };
   __shared__ Smem sm;
   const int lane = __lane_id(), wave = threadIdx.x / kWave;
-  // Workgroup -> (tile, group of draft rows). Workgroup b runs on XCD b % 8;
-  // the groups of one tile take consecutive slots of the same XCD, so that
-  // the tile is read from HBM once and served to the other groups from that
-  // XCD's L2. One group (M <= 64) is the identity map.
-  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
-  const int cg = slot % a.cgroups, tile = xcd + 8 * (slot / a.cgroups);
-  if (tile >= a.tiles) return;
+  const int tile = blockIdx.x;
   const int row0 = tile * kTileRows;
-  const int mb = cg * kGroupRows;               // first draft row of the group
-  const int M = min(kGroupRows, a.M - mb);      // draft rows of the group
+  const int M = a.M;  // draft rows, at most kGroupRows
   const int c16 = a.c16;
   const int g = lane >> 4, r16 = lane & 15;
   // This wave's contiguous range of 16-byte chunks (a multiple of 4).
@@ -891,7 +881,7 @@ void head_mfma_kernel(HeadArgs a) {
     for (int q = 0; q < kStageChunks; ++q)
       v[q] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, off, q * row4_bytes,
-                                                       kShared ? 0 : kCpolNt));
+                                                       kCpolNt));
   };
   // One stage: its loads (v) go to LDS, then the B operands of the whole
   // stage are loaded (contiguous loads from L2), then v is refilled with the
@@ -914,13 +904,13 @@ void head_mfma_kernel(HeadArgs a) {
 #pragma unroll
         for (int cb = 0; cb < NT; ++cb) {
           const int row = cb * 16 + r16;
-          bv[t][cb] = (ok && row < M) ? a.h[(size_t)(mb + row) * c16 + ch] : u32x4{0, 0, 0, 0};
+          bv[t][cb] = (ok && row < M) ? a.h[(size_t)row * c16 + ch] : u32x4{0, 0, 0, 0};
         }
       } else {
-        const u32x4 *hs = a.hp + (size_t)((base / 4 + t) * a.ntt + 4 * cg) * kWave + lane;
+        const u32x4 *hs = a.hp + (size_t)((base / 4 + t) * a.ntt) * kWave + lane;
 #pragma unroll
         for (int cb = 0; cb < NT; ++cb)
-          bv[t][cb] = (ok && 4 * cg + cb < a.ntt) ? hs[cb * kWave] : u32x4{0, 0, 0, 0};
+          bv[t][cb] = (ok && cb < a.ntt) ? hs[cb * kWave] : u32x4{0, 0, 0, 0};
       }
     }
     if constexpr (decltype(prefetch)::value) load_stage(v, base + kStageChunks);
@@ -962,10 +952,10 @@ void head_mfma_kernel(HeadArgs a) {
   __syncthreads();
   // Top-k mode: the sums go straight to the logit buffer, which the row
   // merge reads; sampling mode keeps them in LDS for the tile epilogue.
-  // Streaming stores go through a buffer resource over the group's rows from
+  // Streaming stores go through a buffer resource over the draft rows from
   // this tile on (uniform base, per-lane byte offsets, bounds-checked).
   const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
-      a.zbuf + (size_t)mb * a.zpitch + row0, 0,
+      a.zbuf + row0, 0,
       (int)(((size_t)M * a.zpitch - row0) * 4), kBufferRsrcWord3);
   for (int i = threadIdx.x; i < NT * 16 * (kTileRows / 4); i += kMfmaWaves * kWave) {
     const int row = i / (kTileRows / 4), c4 = 4 * (i % (kTileRows / 4));
@@ -984,7 +974,7 @@ void head_mfma_kernel(HeadArgs a) {
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, val), zrs,
                                                (row * a.zpitch + c4) * 4, 0, kCpolNt);
       else
-        *reinterpret_cast<f32x4 *>(a.zbuf + (size_t)(mb + row) * a.zpitch + row0 + c4) = val;
+        *reinterpret_cast<f32x4 *>(a.zbuf + (size_t)row * a.zpitch + row0 + c4) = val;
     }
   }
   __syncthreads();
@@ -1022,7 +1012,7 @@ void head_mfma_kernel(HeadArgs a) {
         const float mw = qm[w * kWave + lane];
         if (mw != -INFINITY) S += qs[w * kWave + lane] * __expf(mw - mu);
       }
-      a.tile_ms[(size_t)(mb + m) * a.tiles + tile] = pack_ms(mu, S);
+      a.tile_ms[(size_t)m * a.tiles + tile] = pack_ms(mu, S);
     }
   } else {
     const bool valid = row0 + lane < a.V_high;
@@ -1031,12 +1021,12 @@ void head_mfma_kernel(HeadArgs a) {
     // the variates of all four rows.
     for (int b = wave; 4 * b < M; b += kMfmaWaves) {
       const u32x4 x =
-          gumbel_words(a.seed_lo, a.seed_hi, a.off_lo, a.off_hi, mb / 4 + b, row0 + lane);
+          gumbel_words(a.seed_lo, a.seed_hi, a.off_lo, a.off_hi, b, row0 + lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = 4 * b + r;
         if (m < M)
-          wave_publish_sample(a, mb + m, tile, sm.part[0][m][lane], gumbel_from_word(x[r]),
+          wave_publish_sample(a, m, tile, sm.part[0][m][lane], gumbel_from_word(x[r]),
                               fid, valid);
       }
     }
@@ -1299,13 +1289,8 @@ hipError_t launch_mfma(const HeadArgs &a, hipStream_t stream) {
     hipError_t e0 = hipGetLastError();
     if (e0 != hipSuccess) return e0;
   }
-  const int slots = (a.tiles + 7) / 8 * a.cgroups;  // per XCD
-  if (NT == 4 && a.cgroups > 1)
-    hipLaunchKernelGGL((head_mfma_kernel<4, true>), dim3(8 * slots), dim3(kMfmaWaves * kWave),
-                       0, stream, a);
-  else
-    hipLaunchKernelGGL((head_mfma_kernel<NT, false>), dim3(8 * slots),
-                       dim3(kMfmaWaves * kWave), 0, stream, a);
+  hipLaunchKernelGGL((head_mfma_kernel<NT>), dim3(a.tiles), dim3(kMfmaWaves * kWave), 0,
+                     stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.sample)
@@ -1429,7 +1414,6 @@ hipError_t launch_head_call(const uint16_t *h, int32_t M, int32_t d, const uint1
   a.tile_z = reinterpret_cast<uint64_t *>(base + p.off_tile_z);
   a.zbuf = reinterpret_cast<float *>(base + p.off_zbuf);
   a.zpitch = p.tiles * kTileRows;
-  a.cgroups = (M + kGroupRows - 1) / kGroupRows;
   a.zstream = (size_t)M * p.tiles * kTileRows * 4 >= kZStreamBytes ? 1 : 0;
   a.ntt = (M + 15) / 16;
   // Up to kGemvMaxRows rows: one GEMV pass with the merge in the same
