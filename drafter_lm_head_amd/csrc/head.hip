@@ -1370,8 +1370,10 @@ HeadPlan head_plan(int32_t M, int32_t V_high, int32_t k) {
   off += align_up((size_t)M * p.tiles * 8, 256);
   p.off_tile_z = off;  // sampling mode: z of each tile's drawn row
   off += align_up((size_t)M * p.tiles * 8, 256);
-  p.off_hpack = off;  // MFMA path past 32 rows: h in B-operand order, 16 * NT rows x d
-  off += M > 32 ? align_up((size_t)((M + 15) / 16) * 16 * (size_t)VT_D_MAX * 2, 256) : 0;
+  p.off_hpack = off;  // 64-row MFMA path past 32 rows: h in B-operand order, 16 * NT rows x d
+  off += (M > 32 && M <= kGroupRows)
+             ? align_up((size_t)((M + 15) / 16) * 16 * (size_t)VT_D_MAX * 2, 256)
+             : 0;
   p.off_zbuf = off;  // MFMA path, top-k mode: logits [M][tiles * kTileRows] fp32
   off += mfma ? align_up((size_t)M * p.tiles * kTileRows * 4, 256) : 0;
   p.bytes = off;
