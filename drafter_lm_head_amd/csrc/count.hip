@@ -11,6 +11,7 @@
 // table (no global atomics), and a second kernel sums the rows, which keeps
 // the result independent of scheduling.
 #include <algorithm>
+#include <atomic>
 
 #include "vt_internal.hpp"
 
@@ -368,8 +369,14 @@ hipError_t launch_count(const int32_t *ids, uint64_t n, int32_t V,
   unsigned long long *inv = reinterpret_cast<unsigned long long *>(
       static_cast<char *>(ws) + p.partial_bytes);
   const int slots = p.n_ranges * (p.n_chunks / 8);
-  static bool lds_opt_in = false;  // the counting kernels need > 64 KB of LDS
-  if (!lds_opt_in) {
+  // The counting kernels need more than 64 KB of LDS: opt in once per device
+  // (a bit per device; setting the attribute twice is harmless).
+  static std::atomic<uint64_t> lds_opt_in{0};
+  int dev = 0;
+  hipError_t de = hipGetDevice(&dev);
+  if (de != hipSuccess) return de;
+  const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+  if (!bit || !(lds_opt_in.load(std::memory_order_acquire) & bit)) {
     hipError_t a = hipFuncSetAttribute((const void *)count_partial_kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)(kRangeBinsMax * 4));
@@ -380,7 +387,7 @@ hipError_t launch_count(const int32_t *ids, uint64_t n, int32_t V,
                               (int)(kRange16Max * 2));
       if (a != hipSuccess) return a;
     }
-    lds_opt_in = true;
+    lds_opt_in.fetch_or(bit, std::memory_order_release);
   }
   if (p.bins16) {
     uint16_t *partial = static_cast<uint16_t *>(ws);
