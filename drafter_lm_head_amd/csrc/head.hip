@@ -1178,42 +1178,85 @@ void head_gemm_kernel(HeadArgs a) {
   const int trow0 = tile * kTileRows;
   const int mw0 = mrow0 + 64 * wc;  // the wave's first draft row
   if (a.sample) {
-    // Sampling: the wave's block goes to LDS as [draft row][tile row] (the
-    // stage buffers are free once every wave is past its last step), then
-    // the draw runs per tile row as on the 64-row path: one Philox call per
-    // lane and block of four draft rows gives the variates of all four.
-    __syncthreads();
+    // Sampling. Lane (g, r16) holds draft row m = mw0 + 16 cb + r16 at tile
+    // rows j = trow0 + 16 rb + 4 g + i. The four lanes r16 = 4 q .. 4 q + 3
+    // of one g (a quad) share the Philox block m / 4 and the same 16 tile
+    // rows: quad lane r makes the calls of the tile rows (rb, i = r), whose
+    // word s is the variate of the block's draft row s, and three exchanges
+    // within the quad (exchange k: send word r ^ k, receive from lane r ^ k)
+    // give every lane its own row's variates. Each lane then reduces its
+    // draft row over its 16 tile rows, and two cross-lane steps combine the
+    // four lanes that hold one draft row.
     if (tile >= a.tiles) return;
-    float *zs = reinterpret_cast<float *>(&sm[0]) + wave * (kWave * kPartPitch);
+    const int qr = r16 & 3;
+    auto pick4 = [](u32x4 w, int i) -> uint32_t {
+      return i == 0 ? w[0] : i == 1 ? w[1] : i == 2 ? w[2] : w[3];
+    };
+    auto pickf = [](f32x4 w, int i) -> float {
+      return i == 0 ? w[0] : i == 1 ? w[1] : i == 2 ? w[2] : w[3];
+    };
+    int32_t fid[4][4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        f32x4 v = acc[rb][cb];
-        if (a.bias) {
+      for (int i = 0; i < 4; ++i) {
+        const int row = trow0 + 16 * rb + 4 * g + i;
+        fid[rb][i] = row < a.V_high ? a.t2f[row] : 0;
+        if (a.bias && row < a.V_high)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = trow0 + 16 * rb + 4 * g + i;
-            if (row < a.V_high) v[i] += bf16_to_f32(a.bias[row]);
+          for (int cb = 0; cb < 4; ++cb) acc[rb][cb][i] += bf16_to_f32(a.bias[row]);
+      }
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const int m = mw0 + 16 * cb + r16;
+      if (mw0 + 16 * cb >= a.M) break;  // uniform: no row of this block exists
+      uint64_t best = 0;
+      float zb = 0.f, mu = -INFINITY;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const u32x4 w = gumbel_words(a.seed_lo, a.seed_hi, a.off_lo, a.off_hi,
+                                     (uint32_t)(m >> 2), trow0 + 16 * rb + 4 * g + qr);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t x = k == 0 ? pick4(w, qr)
+                                    : (uint32_t)__shfl_xor((int)pick4(w, qr ^ k), k);
+          const int i = qr ^ k;  // tile row (rb, i) of this variate
+          const int32_t f = i == 0 ? fid[rb][0] : i == 1 ? fid[rb][1]
+                          : i == 2 ? fid[rb][2] : fid[rb][3];
+          const float z = pickf(acc[rb][cb], i);
+          if (trow0 + 16 * rb + 4 * g + i < a.V_high) {
+            const uint64_t key = make_key(z + gumbel_from_word(x), f);
+            if (key > best) {
+              best = key;
+              zb = z;
+            }
+            mu = fmaxf(mu, z);
           }
         }
-        *reinterpret_cast<f32x4 *>(zs + (16 * cb + r16) * kPartPitch + 16 * rb + 4 * g) = v;
       }
-    // The wave reads what its own lanes wrote: keep the compiler from
-    // moving the reads up, and let the writes land first.
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    const bool valid = trow0 + lane < a.V_high;
-    const int32_t fid = valid ? a.t2f[trow0 + lane] : 0;
-    for (int b = 0; b < kWave / 4 && mw0 + 4 * b < a.M; ++b) {
-      const u32x4 x =
-          gumbel_words(a.seed_lo, a.seed_hi, a.off_lo, a.off_hi, mw0 / 4 + b, trow0 + lane);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = mw0 + 4 * b + r;
-        if (m < a.M)
-          wave_publish_sample(a, m, tile, zs[(4 * b + r) * kPartPitch + lane],
-                              gumbel_from_word(x[r]), fid, valid);
+      for (int x = 16; x <= 32; x <<= 1) {
+        const uint64_t ob = ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(best >> 32), x) << 32) |
+                            (uint32_t)__shfl_xor((int)(uint32_t)best, x);
+        const float oz = __shfl_xor(zb, x);
+        if (ob > best) {
+          best = ob;
+          zb = oz;
+        }
+        mu = fmaxf(mu, __shfl_xor(mu, x));
+      }
+      float S = 0.f;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (trow0 + 16 * rb + 4 * g + i < a.V_high) S += __expf(acc[rb][cb][i] - mu);
+      S += __shfl_xor(S, 16);
+      S += __shfl_xor(S, 32);
+      if (g == 0 && m < a.M) {
+        publish_u64(a.tile_keys + (size_t)m * a.tiles + tile, best);
+        publish_u64(a.tile_z + (size_t)m * a.tiles + tile, __float_as_uint(zb));
+        publish_u64(a.tile_ms + (size_t)m * a.tiles + tile, pack_ms(mu, S));
       }
     }
     return;
