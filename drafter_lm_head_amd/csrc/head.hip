@@ -1462,7 +1462,9 @@ hipError_t launch_head_call(const uint16_t *h, int32_t M, int32_t d, const uint1
   a.zstream = (size_t)M * p.tiles * kTileRows * 4 >= kZStreamBytes ? 1 : 0;
   a.ntt = (M + 15) / 16;
   // Up to kGemvMaxRows rows: one GEMV pass with the merge in the same
-  // kernel. More rows: the MFMA skinny GEMM, then one merge workgroup per row.
+  // kernel. Up to 64 rows: the MFMA skinny GEMM over one tile per workgroup;
+  // more: the GEMM tiling of 128 x 128 blocks. Then one merge workgroup per
+  // draft row.
   if (M <= kGemvMaxRows) return launch_gemv(a, stream);
   if (M > kGroupRows) return launch_gemm(a, stream);
   switch ((M + 15) / 16) {
