@@ -85,6 +85,79 @@ __device__ __forceinline__ void wave_publish_sample(const HeadArgs &a, int m, in
 }
 
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// The same draw for the 16 draft rows m0 + r16 that a wave holds in the
+// MFMA accumulator layout: lane (g, r16) has z[rb][i], the logit of draft
+// row m0 + r16 at tile row trow0 + 16 rb + 4 g + i, and fid[rb][i], that
+// row's full id. The four lanes r16 = 4 q .. 4 q + 3 of one g (a quad)
+// share the Philox block (m0 + r16) / 4 and the same 16 tile rows: quad
+// lane r makes the calls of the tile rows (rb, i = r), whose word s is the
+// variate of the block's draft row s, and three exchanges within the quad
+// (exchange k: send word r ^ k, receive from lane r ^ k) give every lane
+// its own row's variates. Each lane reduces its draft row over its 16 tile
+// rows and two cross-lane steps combine the four lanes of a row. m0 is a
+// multiple of 16; every lane of the wave must call it.
+__device__ __forceinline__ void quad_draw_publish(const HeadArgs &a, int m0, int tile,
+                                                  int trow0, const f32x4 (&z)[4],
+                                                  const int32_t (&fid)[4][4]) {
+  const int lane = __lane_id(), g = lane >> 4, r16 = lane & 15, qr = r16 & 3;
+  const int m = m0 + r16;
+  auto pick4 = [](u32x4 w, int i) -> uint32_t {
+    return i == 0 ? w[0] : i == 1 ? w[1] : i == 2 ? w[2] : w[3];
+  };
+  auto pickf = [](f32x4 w, int i) -> float {
+    return i == 0 ? w[0] : i == 1 ? w[1] : i == 2 ? w[2] : w[3];
+  };
+  uint64_t best = 0;
+  float zb = 0.f, mu = -INFINITY;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const u32x4 w = gumbel_words(a.seed_lo, a.seed_hi, a.off_lo, a.off_hi, (uint32_t)(m >> 2),
+                                 trow0 + 16 * rb + 4 * g + qr);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t x = k == 0 ? pick4(w, qr) : (uint32_t)__shfl_xor((int)pick4(w, qr ^ k), k);
+      const int i = qr ^ k;  // tile row (rb, i) of this variate
+      const int32_t f = i == 0 ? fid[rb][0] : i == 1 ? fid[rb][1] : i == 2 ? fid[rb][2]
+                                                                          : fid[rb][3];
+      const float zv = pickf(z[rb], i);
+      if (trow0 + 16 * rb + 4 * g + i < a.V_high) {
+        const uint64_t key = make_key(zv + gumbel_from_word(x), f);
+        if (key > best) {
+          best = key;
+          zb = zv;
+        }
+        mu = fmaxf(mu, zv);
+      }
+    }
+  }
+#pragma unroll
+  for (int x = 16; x <= 32; x <<= 1) {
+    const uint64_t ob = ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(best >> 32), x) << 32) |
+                        (uint32_t)__shfl_xor((int)(uint32_t)best, x);
+    const float oz = __shfl_xor(zb, x);
+    if (ob > best) {
+      best = ob;
+      zb = oz;
+    }
+    mu = fmaxf(mu, __shfl_xor(mu, x));
+  }
+  float S = 0.f;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (trow0 + 16 * rb + 4 * g + i < a.V_high) S += __expf(z[rb][i] - mu);
+  S += __shfl_xor(S, 16);
+  S += __shfl_xor(S, 32);
+  if (g == 0 && m < a.M) {
+    publish_u64(a.tile_keys + (size_t)m * a.tiles + tile, best);
+    publish_u64(a.tile_z + (size_t)m * a.tiles + tile, __float_as_uint(zb));
+    publish_u64(a.tile_ms + (size_t)m * a.tiles + tile, pack_ms(mu, S));
+  }
+}
+
 constexpr int kMaxTiles = VT_VHIGH_MAX / kTileRows;
 
 constexpr int kCandCap = 1024;   // survivors the final merge can hold
@@ -797,7 +870,6 @@ __device__ void row_merge(const HeadArgs &a, int m, MergeShared<WAVES> &sh, int3
 // costs hundreds of VALU instructions per (draft row, tile) pair, all of it
 // issued after the streaming ends. Sampling publishes each tile's draw.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMfmaWaves = 4;
 // A logit buffer of this size or more is written with streaming stores: left
@@ -1014,14 +1086,14 @@ void head_mfma_kernel(HeadArgs a) {
       }
       a.tile_ms[(size_t)m * a.tiles + tile] = pack_ms(mu, S);
     }
-  } else {
+  } else if (NT == 1) {
+    // Sampling, up to 16 draft rows: per tile row (lane), draft rows in
+    // blocks of four over the four waves; one Philox call per lane and block
+    // gives the variates of all four rows.
     const bool valid = row0 + lane < a.V_high;
     const int32_t fid = valid ? a.t2f[row0 + lane] : 0;
-    // Draft rows in blocks of four: one Philox call per lane and block gives
-    // the variates of all four rows.
     for (int b = wave; 4 * b < M; b += kMfmaWaves) {
-      const u32x4 x =
-          gumbel_words(a.seed_lo, a.seed_hi, a.off_lo, a.off_hi, b, row0 + lane);
+      const u32x4 x = gumbel_words(a.seed_lo, a.seed_hi, a.off_lo, a.off_hi, b, row0 + lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = 4 * b + r;
@@ -1030,6 +1102,23 @@ void head_mfma_kernel(HeadArgs a) {
                               fid, valid);
       }
     }
+  } else if (16 * wave < M) {
+    // Sampling, more rows: wave w draws for the column block of draft rows
+    // 16 w .. 16 w + 15, reading the tile's logits (bias included) back from
+    // LDS in the accumulator layout for the quad-transposed draw (with one
+    // block the per-row draw above spreads the rows over all four waves).
+    f32x4 z[4];
+    int32_t fid[4][4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      z[rb] = *reinterpret_cast<const f32x4 *>(&sm.part[0][16 * wave + r16][16 * rb + 4 * g]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = row0 + 16 * rb + 4 * g + i;
+        fid[rb][i] = row < a.V_high ? a.t2f[row] : 0;
+      }
+    }
+    quad_draw_publish(a, 16 * wave, tile, row0, z, fid);
   }
 }
 
@@ -1178,23 +1267,8 @@ void head_gemm_kernel(HeadArgs a) {
   const int trow0 = tile * kTileRows;
   const int mw0 = mrow0 + 64 * wc;  // the wave's first draft row
   if (a.sample) {
-    // Sampling. Lane (g, r16) holds draft row m = mw0 + 16 cb + r16 at tile
-    // rows j = trow0 + 16 rb + 4 g + i. The four lanes r16 = 4 q .. 4 q + 3
-    // of one g (a quad) share the Philox block m / 4 and the same 16 tile
-    // rows: quad lane r makes the calls of the tile rows (rb, i = r), whose
-    // word s is the variate of the block's draft row s, and three exchanges
-    // within the quad (exchange k: send word r ^ k, receive from lane r ^ k)
-    // give every lane its own row's variates. Each lane then reduces its
-    // draft row over its 16 tile rows, and two cross-lane steps combine the
-    // four lanes that hold one draft row.
+    // Sampling: the quad-transposed draw per 16-row column block.
     if (tile >= a.tiles) return;
-    const int qr = r16 & 3;
-    auto pick4 = [](u32x4 w, int i) -> uint32_t {
-      return i == 0 ? w[0] : i == 1 ? w[1] : i == 2 ? w[2] : w[3];
-    };
-    auto pickf = [](f32x4 w, int i) -> float {
-      return i == 0 ? w[0] : i == 1 ? w[1] : i == 2 ? w[2] : w[3];
-    };
     int32_t fid[4][4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
@@ -1208,56 +1282,9 @@ void head_gemm_kernel(HeadArgs a) {
       }
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
-      const int m = mw0 + 16 * cb + r16;
       if (mw0 + 16 * cb >= a.M) break;  // uniform: no row of this block exists
-      uint64_t best = 0;
-      float zb = 0.f, mu = -INFINITY;
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const u32x4 w = gumbel_words(a.seed_lo, a.seed_hi, a.off_lo, a.off_hi,
-                                     (uint32_t)(m >> 2), trow0 + 16 * rb + 4 * g + qr);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t x = k == 0 ? pick4(w, qr)
-                                    : (uint32_t)__shfl_xor((int)pick4(w, qr ^ k), k);
-          const int i = qr ^ k;  // tile row (rb, i) of this variate
-          const int32_t f = i == 0 ? fid[rb][0] : i == 1 ? fid[rb][1]
-                          : i == 2 ? fid[rb][2] : fid[rb][3];
-          const float z = pickf(acc[rb][cb], i);
-          if (trow0 + 16 * rb + 4 * g + i < a.V_high) {
-            const uint64_t key = make_key(z + gumbel_from_word(x), f);
-            if (key > best) {
-              best = key;
-              zb = z;
-            }
-            mu = fmaxf(mu, z);
-          }
-        }
-      }
-#pragma unroll
-      for (int x = 16; x <= 32; x <<= 1) {
-        const uint64_t ob = ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(best >> 32), x) << 32) |
-                            (uint32_t)__shfl_xor((int)(uint32_t)best, x);
-        const float oz = __shfl_xor(zb, x);
-        if (ob > best) {
-          best = ob;
-          zb = oz;
-        }
-        mu = fmaxf(mu, __shfl_xor(mu, x));
-      }
-      float S = 0.f;
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (trow0 + 16 * rb + 4 * g + i < a.V_high) S += __expf(acc[rb][cb][i] - mu);
-      S += __shfl_xor(S, 16);
-      S += __shfl_xor(S, 32);
-      if (g == 0 && m < a.M) {
-        publish_u64(a.tile_keys + (size_t)m * a.tiles + tile, best);
-        publish_u64(a.tile_z + (size_t)m * a.tiles + tile, __float_as_uint(zb));
-        publish_u64(a.tile_ms + (size_t)m * a.tiles + tile, pack_ms(mu, S));
-      }
+      const f32x4 z[4] = {acc[0][cb], acc[1][cb], acc[2][cb], acc[3][cb]};
+      quad_draw_publish(a, mw0 + 16 * cb, tile, trow0, z, fid);
     }
     return;
   }
