@@ -98,19 +98,59 @@ def recorded_traffic():
     return int(fields["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(h, Wt, t2f, k, budget_s=12.0):
+def cpu_info():
+    """(usable host cores, CPU model string)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return len(os.sched_getaffinity(0)), model
+
+
+def cpu_baseline(h, Wt, t2f, k, budget_s=8.0):
+    """The unmodified oracle's full draft-head call on the host cores: with
+    every OpenMP thread it uses by default and with one thread."""
     import oracle
     oracle.draft_head(h[:1], Wt[:64], t2f[:64], 1)      # load + page in
-    n, t0 = 0, time.perf_counter()
-    while True:
-        oracle.draft_head(h, Wt, t2f, k)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    return {"value": n / el, "unit": "calls/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": f"{n} full draft-head calls (fp64 C oracle, OpenMP over rows) "
-                      f"on the same inputs, {el:.1f} s"}
+    nproc, model = cpu_info()
+
+    def run(budget):
+        ts, t0 = [], time.perf_counter()
+        while True:
+            a = time.perf_counter()
+            oracle.draft_head(h, Wt, t2f, k)
+            ts.append(time.perf_counter() - a)
+            if time.perf_counter() - t0 >= budget and len(ts) >= 3:
+                break
+        return len(ts), sum(ts), statistics.median(ts)
+
+    t_all = oracle.threads()
+    n, el, med = run(budget_s)
+    oracle.set_threads(1)
+    n1, el1, med1 = run(budget_s)
+    oracle.set_threads(t_all)
+    return {"value": n / el, "unit": "calls/s", "cores": t_all, "kind": "oracle",
+            "sample": f"{n} full draft-head calls (fp64 C oracle, OpenMP over rows, {t_all} "
+                      f"threads) on the same inputs, {el:.1f} s",
+            "median_ms_per_call": round(1000 * med, 3),
+            "t1": {"value": n1 / el1, "unit": "calls/s", "cores": 1,
+                   "median_ms_per_call": round(1000 * med1, 3),
+                   "sample": f"{n1} calls with one thread, {el1:.1f} s"},
+            "nproc": nproc, "cpu_model": model}
+
+
+def interleaved_us(fa, fb, n, rounds, torch):
+    """Median µs per call of two call sequences timed in alternating batches."""
+    ta, tb = [], []
+    for _ in range(rounds):
+        ta.append(1000.0 * time_calls(fa, n, torch) / n)
+        tb.append(1000.0 * time_calls(fb, n, torch) / n)
+    return statistics.median(ta), statistics.median(tb)
 
 
 def main():
@@ -230,6 +270,44 @@ def main():
     ms_sample = time_calls(cold_sample, args.steps, torch) / args.steps
     log(f"sample (cold): {ms_sample * 1000:.2f} us/step")
 
+    # practical ceiling: a plain streaming read of the same W_trim copies
+    sink = torch.zeros(1, dtype=torch.int64, device=dev)
+    read = lambda i: dlh.vt_stream_read(copies[i % R], sink)
+    for i in range(50):
+        read(i)
+    us_read = 1000.0 * time_calls(read, args.steps, torch) / args.steps
+    log(f"streaming read of W_trim (cold): {us_read:.2f} us/call")
+
+    # the remap's cost: the same call returning trimmed indices, interleaved
+    t_ids = torch.empty((M, k), dtype=torch.int32, device=dev)
+    t_p = torch.empty((M, k), dtype=torch.float32, device=dev)
+    ws_t = torch.zeros(dlh.vt_draft_head_workspace_size(M, V_high, d, k), dtype=torch.uint8,
+                       device=dev)
+    trimmed = lambda i: dlh.vt_draft_head_trimmed(h, copies[i % R], k, trimmed_ids=t_ids,
+                                                  probs=t_p, ws=ws_t)
+    for i in range(50):
+        trimmed(i)
+    us_remap, us_noremap = interleaved_us(cold, trimmed, max(200, args.steps // 4), 5, torch)
+    log(f"remap: {us_remap:.2f} us with, {us_noremap:.2f} us without")
+
+    # the same cold calls replayed from a captured graph (no per-call launch)
+    n_graph = 4 * R
+    gstream = torch.cuda.Stream()
+    gstream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(gstream):
+        for i in range(n_graph):
+            cold(i)
+    torch.cuda.current_stream().wait_stream(gstream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(n_graph):
+            cold(i)
+    graph.replay()
+    reps = max(1, args.steps // n_graph)
+    us_graph = 1000.0 * time_calls(lambda i: graph.replay(), reps, torch) / (reps * n_graph)
+    log(f"graph replay: {us_graph:.2f} us/call")
+
     # pipeline: one pass of every step (count, select, gather, draft head)
     def pipeline():
         dlh.vt_count_freq(ids, w.V, counts=counts, n_invalid=n_inv)
@@ -303,6 +381,19 @@ def main():
                      "us_per_launch": round(ms_step * 1000, 3),
                      "us_single_launch_events": round(us_launch, 3)},
         "cpu_baseline": cpu,
+        "ceiling": {"what": "vt_stream_read: plain 16-byte non-temporal streaming read of the "
+                            "same W_trim copies (cold), the practical bandwidth ceiling",
+                    "bytes_per_call": wt_bytes, "us_per_call": round(us_read, 3),
+                    "GB_per_s": round(wt_bytes / (us_read * 1e-6) / 1e9, 1),
+                    "frac_of_peak": round(wt_bytes / (us_read * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                    "head_over_ceiling": round(ms_step * 1000 / us_read, 4)},
+        "remap": {"what": "vt_draft_head (full ids through t2f) against vt_draft_head_trimmed "
+                          "(trimmed indices), interleaved, cold",
+                  "us_with_remap": round(us_remap, 3), "us_without_remap": round(us_noremap, 3),
+                  "overhead_frac": round((us_remap - us_noremap) / us_noremap, 5)},
+        "graph": {"what": f"{n_graph} cold calls captured in one graph, replayed",
+                  "us_per_call": round(us_graph, 3),
+                  "GB_per_s": round(nb / (us_graph * 1e-6) / 1e9, 1)},
         "warm": {"us_per_call": round(ms_warm * 1000, 3),
                  "GB_per_s": round(nb / (ms_warm * 1e-3) / 1e9, 1)},
         "sample": {"us_per_call": round(ms_sample * 1000, 3),

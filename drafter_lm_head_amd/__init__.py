@@ -11,7 +11,14 @@ stream. The functions keep the C names:
 * ``vt_draft_head(h, W_trim, t2f, k)`` -> (full_ids int32[M, k], probs f32[M, k])
 * ``vt_draft_head_bias(h, W_trim, bias, t2f, k)``, ``vt_draft_sample(...)``,
   ``vt_draft_sample_bias(...)``: the same with a bias, or one draw per row
-* ``vt_head_logits(h, W_trim)``        -> logits f32[M, V_high] (checks only)
+* ``vt_head_logits(h, W_trim)``        -> logits f32[M, V_high] (checks only),
+  with ``stats=True`` also (row_max f32[M], row_sum f32[M])
+* ``vt_draft_head_trimmed(h, W_trim, k)`` -> (trimmed_ids, probs): the draft
+  step without the remap (measures the remap's cost)
+* ``vt_draft_head_status(ws)``         -> raises VtError if a bounded wait in a
+  kernel gave up since the last query (host-blocking)
+* ``vt_stream_read(buf)``              : a plain streaming read of a buffer
+  (the draft head's practical bandwidth ceiling)
 
 bfloat16 arrays may be passed as ``torch.bfloat16`` or as their 16-bit
 patterns (``torch.int16`` / ``torch.uint16``). Results stay on the device;
@@ -33,13 +40,17 @@ __all__ = [
     "vt_gather_bias", "vt_draft_head_bias", "vt_draft_sample_bias",
     "vt_select_vocab_workspace_size", "vt_draft_head_workspace_size",
     "coverage", "vt_coverage_curve", "vt_coverage_curve_workspace_size",
+    "vt_draft_head_trimmed", "vt_draft_head_status", "vt_stream_read",
+    "VT_WS_ERROR_OFFSET", "VT_WS_HOLD_OFFSET", "VT_WS_SPIN_LIMIT_OFFSET",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libvocabtrim.so")
 
 VT_OK, VT_ERR_INVALID_ARG, VT_ERR_UNSUPPORTED, VT_ERR_WORKSPACE, VT_ERR_HIP = 0, -1, -2, -3, -4
+VT_ERR_TIMEOUT = -5
 VT_K_MAX, VT_M_MAX, VT_D_MAX, VT_VHIGH_MAX = 64, 512, 8192, 262144
+VT_WS_ERROR_OFFSET, VT_WS_HOLD_OFFSET, VT_WS_SPIN_LIMIT_OFFSET = 128, 132, 136
 
 _lock = threading.Lock()
 _lib = None
@@ -60,7 +71,10 @@ _SIGS = {
     "vt_draft_head_bias": (_INT, [_P, _I32, _I32, _P, _P, _I32, _P, _I32, _P, _P, _P, _SZ, _P]),
     "vt_draft_sample_bias": (_INT, [_P, _I32, _I32, _P, _P, _I32, _P, _U64, _U64, _P, _P, _P, _SZ,
                                     _P]),
-    "vt_head_logits": (_INT, [_P, _I32, _I32, _P, _I32, _P, _P]),
+    "vt_head_logits": (_INT, [_P, _I32, _I32, _P, _I32, _P, _P, _P, _P]),
+    "vt_draft_head_trimmed": (_INT, [_P, _I32, _I32, _P, _I32, _I32, _P, _P, _P, _SZ, _P]),
+    "vt_draft_head_status": (_INT, [_P, _P]),
+    "vt_stream_read": (_INT, [_P, _SZ, _P, _P]),
     "vt_coverage_curve_workspace_size": (_SZ, [_I32, _I32]),
     "vt_coverage_curve": (_INT, [_P, _I32, _P, _I32, C.c_double, _P, _P, _P, _P, _SZ, _P]),
 }
@@ -116,13 +130,20 @@ def _dev(t: torch.Tensor, name: str, dtypes, ndim: int | None = None):
 
 _BF16 = (torch.bfloat16, torch.int16, torch.uint16)
 
-# One cached workspace per (device, kind); grown on demand. The draft-head
+# Cached workspaces, one per (device, stream, kind), grown on demand. Keyed by
+# stream because calls that share a workspace must run in stream order; a
+# buffer replaced by a larger one is released to torch's caching allocator,
+# which reuses it only in the order of that same stream. The draft-head
 # workspace is zero-filled when allocated, as the C ABI requires.
 _ws_cache: dict = {}
 
 
 def _workspace(device: torch.device, kind: str, nbytes: int, zero: bool) -> torch.Tensor:
-    key = (device.index, kind)
+    if torch.cuda.is_current_stream_capturing():
+        raise RuntimeError(f"pass an explicit {kind} workspace (ws=...) when capturing a graph: "
+                           "an implicit one may be reallocated after the capture")
+    stream = torch.cuda.current_stream(device).cuda_stream
+    key = (device.index, stream, kind)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
         n = max(nbytes, 256)
@@ -331,8 +352,10 @@ def _draft_sample(h, W_trim, bias, t2f, seed, offset, full_ids, probs, ws):
 
 
 def vt_head_logits(h: torch.Tensor, W_trim: torch.Tensor,
-                   out: torch.Tensor | None = None) -> torch.Tensor:
-    """fp32 trimmed logits [M, V_high] (parity diagnostics)."""
+                   out: torch.Tensor | None = None, stats: bool = False):
+    """fp32 trimmed logits [M, V_high] (parity diagnostics); with
+    ``stats=True`` returns (logits, row_max[M], row_sum[M]), the subset
+    softmax statistics of each row."""
     _dev(h, "h", _BF16, 2)
     _dev(W_trim, "W_trim", _BF16, 2)
     M, d = h.shape
@@ -342,9 +365,60 @@ def vt_head_logits(h: torch.Tensor, W_trim: torch.Tensor,
     if out is None:
         out = torch.empty((M, V_high), dtype=torch.float32, device=h.device)
     _dev(out, "out", (torch.float32,))
-    _check(lib().vt_head_logits(_ptr(h), M, d, _ptr(W_trim), V_high, _ptr(out), _stream(h)),
-           "vt_head_logits")
-    return out
+    if out.numel() != M * V_high:
+        raise ValueError("out must hold M * V_high entries")
+    rmax = torch.empty(M, dtype=torch.float32, device=h.device) if stats else None
+    rsum = torch.empty(M, dtype=torch.float32, device=h.device) if stats else None
+    _check(lib().vt_head_logits(_ptr(h), M, d, _ptr(W_trim), V_high, _ptr(out), _ptr(rmax),
+                                _ptr(rsum), _stream(h)), "vt_head_logits")
+    return (out, rmax, rsum) if stats else out
+
+
+def vt_draft_head_trimmed(h: torch.Tensor, W_trim: torch.Tensor, k: int,
+                          trimmed_ids: torch.Tensor | None = None,
+                          probs: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """The draft step without the remap: (trimmed_ids[M, k], probs[M, k])."""
+    _dev(h, "h", _BF16, 2)
+    _dev(W_trim, "W_trim", _BF16, 2)
+    M, d = h.shape
+    V_high = W_trim.shape[0]
+    if W_trim.shape[1] != d:
+        raise ValueError("shape mismatch between h and W_trim")
+    dev = h.device
+    if trimmed_ids is None:
+        trimmed_ids = torch.empty((M, k), dtype=torch.int32, device=dev)
+    if probs is None:
+        probs = torch.empty((M, k), dtype=torch.float32, device=dev)
+    _dev(trimmed_ids, "trimmed_ids", (torch.int32,))
+    _dev(probs, "probs", (torch.float32,))
+    if trimmed_ids.numel() != M * k or probs.numel() != M * k:
+        raise ValueError("outputs must hold M * k entries")
+    if ws is None:
+        ws = _workspace(dev, "head", vt_draft_head_workspace_size(M, V_high, d, k), True)
+    _check(lib().vt_draft_head_trimmed(_ptr(h), M, d, _ptr(W_trim), V_high, k,
+                                       _ptr(trimmed_ids), _ptr(probs), _ptr(ws), ws.numel(),
+                                       _stream(h)), "vt_draft_head_trimmed")
+    return trimmed_ids, probs
+
+
+def vt_draft_head_status(ws: torch.Tensor) -> None:
+    """Raises VtError(VT_ERR_TIMEOUT) if a bounded wait inside a kernel that
+    used this draft-head workspace gave up since the last query (clearing
+    the flag). Blocks the host until the stream's work is done."""
+    _dev(ws, "ws", (torch.uint8,), 1)
+    _check(lib().vt_draft_head_status(_ptr(ws), _stream(ws)), "vt_draft_head_status")
+
+
+def vt_stream_read(buf: torch.Tensor, sink: torch.Tensor | None = None) -> torch.Tensor:
+    """A plain streaming read of ``buf`` (16-byte aligned, size a multiple of
+    16 bytes): the practical ceiling of the draft head."""
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise TypeError("buf must be a contiguous device tensor")
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int64, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().vt_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(buf)), "vt_stream_read")
+    return sink
 
 
 def vt_coverage_curve_workspace_size(V: int, L: int) -> int:

@@ -20,7 +20,8 @@ LIB_NAME = "libvocabtrim.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "count.hip", "select.hip", "gather.hip", "head.hip", "coverage.hip"]
+SOURCES = ["api.hip", "count.hip", "select.hip", "gather.hip", "head.hip", "coverage.hip",
+           "stream.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -39,6 +39,7 @@ const char *vt_status_string(int status) {
     case VT_ERR_UNSUPPORTED: return "size beyond the library's limits";
     case VT_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case VT_ERR_HIP: return "HIP launch failed";
+    case VT_ERR_TIMEOUT: return "a bounded wait inside a kernel gave up (outputs hold -1 / NaN)";
     default: return "unknown status";
   }
 }
@@ -203,14 +204,52 @@ int vt_draft_sample_bias(const uint16_t *h, int32_t M, int32_t d,
                                             full_ids, probs, ws, as_stream(stream)));
 }
 
+int vt_draft_head_trimmed(const uint16_t *h, int32_t M, int32_t d,
+                          const uint16_t *W_trim, int32_t V_high, int32_t k,
+                          int32_t *trimmed_ids, float *probs, void *ws,
+                          size_t ws_bytes, void *stream) {
+  int st = check_head(h, M, d, W_trim, V_high);
+  if (st != VT_OK) return st;
+  if (!trimmed_ids || !probs) return VT_ERR_INVALID_ARG;
+  if (k <= 0 || k > V_high) return VT_ERR_INVALID_ARG;
+  if (k > VT_K_MAX) return VT_ERR_UNSUPPORTED;
+  if (!ws || !aligned(ws, 256) ||
+      ws_bytes < vt_draft_head_workspace_size(M, V_high, d, k))
+    return VT_ERR_WORKSPACE;
+  return hip_status(vt::launch_draft_head(h, M, d, W_trim, nullptr, V_high, nullptr, k,
+                                          trimmed_ids, probs, ws, as_stream(stream),
+                                          /*remap=*/false));
+}
+
+int vt_draft_head_status(const void *ws, void *stream) {
+  if (!ws) return VT_ERR_INVALID_ARG;
+  const hipStream_t s = as_stream(stream);
+  char *word = static_cast<char *>(const_cast<void *>(ws)) + VT_WS_ERROR_OFFSET;
+  uint32_t v = 0;
+  if (hipMemcpyAsync(&v, word, sizeof v, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return hip_status(hipErrorUnknown);
+  if (v == 0) return VT_OK;
+  const uint32_t zero = 0;
+  if (hipMemcpyAsync(word, &zero, sizeof zero, hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return hip_status(hipErrorUnknown);
+  return VT_ERR_TIMEOUT;
+}
+
 int vt_head_logits(const uint16_t *h, int32_t M, int32_t d,
                    const uint16_t *W_trim, int32_t V_high, float *logits,
-                   void *stream) {
+                   float *row_max, float *row_sum, void *stream) {
   int st = check_head(h, M, d, W_trim, V_high);
   if (st != VT_OK) return st;
   if (!logits) return VT_ERR_INVALID_ARG;
-  return hip_status(
-      vt::launch_head_logits(h, M, d, W_trim, V_high, logits, as_stream(stream)));
+  return hip_status(vt::launch_head_logits(h, M, d, W_trim, V_high, logits, row_max, row_sum,
+                                           as_stream(stream)));
+}
+
+int vt_stream_read(const void *p, size_t bytes, uint64_t *sink, void *stream) {
+  if (!p || !sink || bytes == 0 || bytes % 16 != 0 || !aligned(p, 16)) return VT_ERR_INVALID_ARG;
+  return hip_status(vt::launch_stream_read(p, bytes, sink, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -15,6 +15,8 @@
 //     depend on scheduling; it writes full_ids and probs.
 // The kernel is bound by HBM bandwidth: it moves 2 * V_high * d bytes of
 // W_trim and does 2 * M * V_high * d flops.
+#include <algorithm>
+
 #include "vt_internal.hpp"
 #include "vocabtrim.h"
 
@@ -51,6 +53,8 @@ struct HeadArgs {
   uint32_t seed_lo, seed_hi, off_lo, off_hi;
   uint64_t *tile_z;      // [M][tiles]: bits of z of each tile's drawn row
   const uint16_t *bias;  // bf16[V_high] added to every logit, or nullptr
+  int32_t remap;         // 1: keys carry t2f[j] (full ids); 0: the trimmed index j
+  uint32_t *status;      // the workspace's fixed words (error, hold, spin limit)
   int32_t ntt;           // MFMA path: 16-row column blocks over all M rows
   float *zbuf;           // MFMA path, top-k mode: logits [M][zpitch]
   int32_t zpitch;        // tiles * kTileRows floats
@@ -61,6 +65,12 @@ __device__ __forceinline__ uint64_t pack_ms(float mu, float S) {
 }
 __device__ __forceinline__ float ms_max(uint64_t v) { return __uint_as_float((uint32_t)v); }
 __device__ __forceinline__ float ms_sum(uint64_t v) { return __uint_as_float((uint32_t)(v >> 32)); }
+
+// Id that a kept row j carries into the keys and the outputs: its full id
+// t2f[j] (the remap), or j itself when the caller asks for trimmed indices.
+__device__ __forceinline__ int32_t fid_at(const HeadArgs &a, int j) {
+  return a.remap ? a.t2f[j] : j;
+}
 
 // Sampling-mode tile partial of one draft row, by one wave (lane = tile row,
 // g = its Gumbel variate): the tile's largest sampling key, (z + g) in key
@@ -500,14 +510,39 @@ __device__ void final_merge(const HeadArgs &a, int m, MergeShared<SW> &sh) {
 // barrier).
 constexpr uint32_t kArriveWaitMax = 1u << 20;
 
-__device__ __forceinline__ void wait_arrivals(const uint32_t *counter, uint32_t n) {
+// Waits until n workgroups have taken a ticket. Returns false if it gave up
+// (after kArriveWaitMax sleeps, or the workspace's spin-limit word when that
+// is nonzero); it then raises the workspace's error word, which
+// vt_draft_head_status reports. The workspace's hold word, zero unless a
+// test sets it, adds that many arrivals that never come. Every thread must
+// call it (it has a barrier); the result is uniform.
+__device__ __forceinline__ bool wait_arrivals(const HeadArgs &a, uint32_t n, uint32_t *s_ok) {
   if (threadIdx.x == 0) {
+    const uint32_t hold = a.status[kWsHold / 4];
+    const uint32_t lim = a.status[kWsSpinLimit / 4] ? a.status[kWsSpinLimit / 4] : kArriveWaitMax;
+    const uint32_t want = n + hold;
     uint32_t spins = 0;
-    while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n &&
-           ++spins < kArriveWaitMax)
+    bool ok;
+    while (!(ok = __hip_atomic_load(a.counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
+                  want) &&
+           ++spins < lim)
       __builtin_amdgcn_s_sleep(2);
+    if (!ok)
+      __hip_atomic_store(a.status + kWsError / 4, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_ok = ok ? 1u : 0u;
   }
   __syncthreads();
+  return *s_ok != 0;
+}
+
+// Outputs of a draft row whose merge could not be trusted: id -1, NaN
+// probabilities (k entries, or one when sampling).
+__device__ __forceinline__ void write_sentinel(const HeadArgs &a, int m) {
+  const int n = a.sample ? 1 : a.k;
+  for (int r = threadIdx.x; r < n; r += blockDim.x) {
+    a.full_ids[(size_t)m * n + r] = -1;
+    if (a.probs) a.probs[(size_t)m * n + r] = __builtin_nanf("");
+  }
 }
 
 // The last of R mergers to finish returns the ticket counter (and the count
@@ -539,7 +574,7 @@ __global__ __launch_bounds__(WAVES *kWave) void head_gemv_kernel(HeadArgs a) {
   static_assert(kTiles * MT <= WAVES, "one wave per (tile, draft row) in the epilogue");
   __shared__ float s_z[MT][kRows];
   __shared__ MergeShared<WAVES> sh;
-  __shared__ uint32_t s_slot, s_next;
+  __shared__ uint32_t s_slot, s_next, s_ok;
 
   const int lane = __lane_id(), wave = threadIdx.x / kWave;
   const int tile0 = blockIdx.x * kTiles, row0 = tile0 * kTileRows;
@@ -552,7 +587,7 @@ __global__ __launch_bounds__(WAVES *kWave) void head_gemv_kernel(HeadArgs a) {
   const bool e_on = wave < kTiles * MT && tile0 + e_sub < a.tiles;
   const int e_row = row0 + e_sub * kTileRows + lane;
   int32_t fid = 0;
-  if (!LOGITS && e_on && e_row < a.V_high) fid = a.t2f[e_row];
+  if (!LOGITS && e_on && e_row < a.V_high) fid = fid_at(a, e_row);
 
   if (threadIdx.x == 0) s_next = WAVES;  // unit w < WAVES is wave w's first
   __syncthreads();
@@ -644,8 +679,13 @@ __global__ __launch_bounds__(WAVES *kWave) void head_gemv_kernel(HeadArgs a) {
     }
     const int R = min(MT, (int)gridDim.x), q = (int)gridDim.x - 1 - (int)ticket;
     if (q >= R) return;
-    if (q > 0) wait_arrivals(a.counter, gridDim.x);
-    for (int m = q; m < MT; m += R) sample_merge<WAVES>(a, m, sh);
+    const bool ok = q == 0 || wait_arrivals(a, gridDim.x, &s_ok);
+    for (int m = q; m < MT; m += R) {
+      if (ok)
+        sample_merge<WAVES>(a, m, sh);
+      else
+        write_sentinel(a, m);
+    }
     finish_merge(a, R);
     return;
   }
@@ -694,8 +734,13 @@ __global__ __launch_bounds__(WAVES *kWave) void head_gemv_kernel(HeadArgs a) {
   }
   const int R = min(MT, (int)gridDim.x), q = (int)gridDim.x - 1 - (int)ticket;
   if (q >= R || wave >= MW) return;
-  if (q > 0) wait_arrivals(a.counter, gridDim.x);
-  for (int m = q; m < MT; m += R) final_merge<MW, WAVES>(a, m, sh);
+  const bool ok = q == 0 || wait_arrivals(a, gridDim.x, &s_ok);
+  for (int m = q; m < MT; m += R) {
+    if (ok)
+      final_merge<MW, WAVES>(a, m, sh);
+    else
+      write_sentinel(a, m);
+  }
   finish_merge(a, R);
 }
 
@@ -799,7 +844,7 @@ __device__ void row_merge(const HeadArgs &a, int m, MergeShared<WAVES> &sh, int3
     for (int i = 0; i < kRound; ++i)
       if (jv[i] < V && ord_from_f32(zv[i]) >= T) {
         const uint32_t pos = atomicAdd(&sh.cnt, 1u);
-        if (pos < (uint32_t)kCandCap) sh.cand[pos] = make_key(zv[i], a.t2f[jv[i]]);
+        if (pos < (uint32_t)kCandCap) sh.cand[pos] = make_key(zv[i], fid_at(a, jv[i]));
       }
   }
   __syncthreads();
@@ -831,7 +876,7 @@ __device__ void row_merge(const HeadArgs &a, int m, MergeShared<WAVES> &sh, int3
         if (j < V) {
           const float z = zr[j];
           if (ord_from_f32(z) >= T) {
-            const uint64_t kv = make_key(z, a.t2f[j]);
+            const uint64_t kv = make_key(z, fid_at(a, j));
             if (kv < prev) best = max_u64(best, kv);
           }
         }
@@ -1091,7 +1136,7 @@ void head_mfma_kernel(HeadArgs a) {
     // blocks of four over the four waves; one Philox call per lane and block
     // gives the variates of all four rows.
     const bool valid = row0 + lane < a.V_high;
-    const int32_t fid = valid ? a.t2f[row0 + lane] : 0;
+    const int32_t fid = valid ? fid_at(a, row0 + lane) : 0;
     for (int b = wave; 4 * b < M; b += kMfmaWaves) {
       const u32x4 x = gumbel_words(a.seed_lo, a.seed_hi, a.off_lo, a.off_hi, b, row0 + lane);
 #pragma unroll
@@ -1115,7 +1160,7 @@ void head_mfma_kernel(HeadArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = row0 + 16 * rb + 4 * g + i;
-        fid[rb][i] = row < a.V_high ? a.t2f[row] : 0;
+        fid[rb][i] = row < a.V_high ? fid_at(a, row) : 0;
       }
     }
     quad_draw_publish(a, 16 * wave, tile, row0, z, fid);
@@ -1275,7 +1320,7 @@ void head_gemm_kernel(HeadArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = trow0 + 16 * rb + 4 * g + i;
-        fid[rb][i] = row < a.V_high ? a.t2f[row] : 0;
+        fid[rb][i] = row < a.V_high ? fid_at(a, row) : 0;
         if (a.bias && row < a.V_high)
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb) acc[rb][cb][i] += bf16_to_f32(a.bias[row]);
@@ -1421,13 +1466,21 @@ hipError_t launch_gemv(const HeadArgs &a, hipStream_t stream) {
 
 static_assert(kDirectH<2> && !kDirectH<3>, "packed h is allocated for more than 32 rows");
 
+// Counters and status words (256 bytes), then the GEMV path's group maxima.
+constexpr size_t head_zero_prefix = 256;
+static_assert(kWsSpinLimit + 4 <= head_zero_prefix, "status words inside the prefix");
+
+size_t head_zero_bytes() {
+  return head_zero_prefix + (size_t)kGemvMaxRows * 2 * kGroups * 8;
+}
+
 HeadPlan head_plan(int32_t M, int32_t V_high, int32_t k) {
   // Fixed-offset prefix that every call leaves at zero: the ticket counter
   // (byte 0), the count of finished row mergers (byte 64), then the group
   // maxima of the GEMV path's draft rows. Per-call data after.
   HeadPlan p;
   p.tiles = (V_high + kTileRows - 1) / kTileRows;
-  size_t off = 256;
+  size_t off = head_zero_prefix;
   p.off_group = off;
   off += (size_t)kGemvMaxRows * 2 * kGroups * 8;
   p.zero_bytes = off;
@@ -1455,7 +1508,7 @@ hipError_t launch_head_call(const uint16_t *h, int32_t M, int32_t d, const uint1
                             const uint16_t *bias, int32_t V_high, const int32_t *t2f,
                             int32_t k, int32_t *full_ids,
                             float *probs, void *ws, bool sample, uint64_t seed,
-                            uint64_t offset, hipStream_t stream) {
+                            uint64_t offset, bool remap, hipStream_t stream) {
   const HeadPlan p = head_plan(M, V_high, k);
   char *base = static_cast<char *>(ws);
   HeadArgs a{};
@@ -1466,8 +1519,10 @@ hipError_t launch_head_call(const uint16_t *h, int32_t M, int32_t d, const uint1
   a.V_high = V_high;
   a.k = k;
   a.tiles = p.tiles;
-  a.counter = reinterpret_cast<uint32_t *>(base);
-  a.merged = reinterpret_cast<uint32_t *>(base + 64);
+  a.counter = reinterpret_cast<uint32_t *>(base + kWsTicket);
+  a.merged = reinterpret_cast<uint32_t *>(base + kWsMerged);
+  a.status = reinterpret_cast<uint32_t *>(base);
+  a.remap = remap ? 1 : 0;
   a.tile_keys = reinterpret_cast<uint64_t *>(base + p.off_tile_keys);
   a.tile_ms = reinterpret_cast<uint64_t *>(base + p.off_tile_ms);
   a.group_max = reinterpret_cast<uint64_t *>(base + p.off_group);
@@ -1506,9 +1561,9 @@ hipError_t launch_head_call(const uint16_t *h, int32_t M, int32_t d, const uint1
 hipError_t launch_draft_head(const uint16_t *h, int32_t M, int32_t d,
                              const uint16_t *W_trim, const uint16_t *bias, int32_t V_high,
                              const int32_t *t2f, int32_t k, int32_t *full_ids,
-                             float *probs, void *ws, hipStream_t stream) {
+                             float *probs, void *ws, hipStream_t stream, bool remap) {
   return launch_head_call(h, M, d, W_trim, bias, V_high, t2f, k, full_ids, probs, ws, false, 0,
-                          0, stream);
+                          0, remap, stream);
 }
 
 hipError_t launch_draft_sample(const uint16_t *h, int32_t M, int32_t d,
@@ -1516,12 +1571,60 @@ hipError_t launch_draft_sample(const uint16_t *h, int32_t M, int32_t d,
                                const int32_t *t2f, uint64_t seed, uint64_t offset,
                                int32_t *full_ids, float *probs, void *ws, hipStream_t stream) {
   return launch_head_call(h, M, d, W_trim, bias, V_high, t2f, 1, full_ids, probs, ws, true,
-                          seed, offset, stream);
+                          seed, offset, true, stream);
+}
+
+namespace {
+// Per-row softmax statistics of logits already in memory (the logits-only
+// check call): mu = max_j z[m, j], S = sum_j exp(z[m, j] - mu), one
+// workgroup per row. Each thread takes the indices tid, tid + 256, ... in
+// order; the waves and then the workgroup combine in a fixed order.
+constexpr int kStatWaves = 4;
+__global__ __launch_bounds__(kStatWaves *kWave) void row_stats_kernel(const float *__restrict__ z,
+                                                                      int n, float *row_max,
+                                                                      float *row_sum) {
+  __shared__ float s_m[kStatWaves], s_s[kStatWaves];
+  const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
+  const float *zr = z + (size_t)blockIdx.x * n;
+  float mu = -INFINITY;
+  for (int j = tid; j < n; j += kStatWaves * kWave) mu = fmaxf(mu, zr[j]);
+  mu = wave_max(mu);
+  if (lane == 0) s_m[wave] = mu;
+  __syncthreads();
+  mu = s_m[0];
+  for (int w = 1; w < kStatWaves; ++w) mu = fmaxf(mu, s_m[w]);
+  float S = 0.f;
+  for (int j = tid; j < n; j += kStatWaves * kWave) S += __expf(zr[j] - mu);
+  S = wave_sum(S);
+  if (lane == 0) s_s[wave] = S;
+  __syncthreads();
+  if (tid == 0) {
+    float t = 0.f;
+    for (int w = 0; w < kStatWaves; ++w) t += s_s[w];
+    if (row_max) row_max[blockIdx.x] = mu;
+    if (row_sum) row_sum[blockIdx.x] = t;
+  }
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(u32x4 *p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    p[i] = u32x4{0, 0, 0, 0};
+}
+}  // namespace
+
+hipError_t launch_zero(void *p, size_t n, hipStream_t stream) {
+  const size_t n16 = n / 16;
+  if (n16 == 0) return hipSuccess;
+  const int blocks = (int)std::min<size_t>((n16 + 255) / 256, 1024);
+  hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<u32x4 *>(p),
+                     n16);
+  return hipGetLastError();
 }
 
 hipError_t launch_head_logits(const uint16_t *h, int32_t M, int32_t d,
                               const uint16_t *W_trim, int32_t V_high,
-                              float *logits, hipStream_t stream) {
+                              float *logits, float *row_max, float *row_sum,
+                              hipStream_t stream) {
   HeadArgs a{};
   a.W = reinterpret_cast<const u32x4 *>(W_trim);
   a.c16 = d / 8;
@@ -1534,6 +1637,11 @@ hipError_t launch_head_logits(const uint16_t *h, int32_t M, int32_t d,
     c.logits = logits + (size_t)m * V_high;
     hipError_t e = launch_cpl<1, true>(c, stream);
     if (e != hipSuccess) return e;
+  }
+  if (row_max || row_sum) {
+    hipLaunchKernelGGL(row_stats_kernel, dim3(M), dim3(kStatWaves * kWave), 0, stream, logits,
+                       V_high, row_max, row_sum);
+    return hipGetLastError();
   }
   return hipSuccess;
 }

@@ -5,6 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "vocabtrim.h"
 #include "vt_device.hpp"
 
 namespace vt {
@@ -42,17 +43,30 @@ hipError_t launch_gather(const uint16_t *W, int32_t V, int32_t d,
 // Draft head: tiles of kTileRows rows of W_trim; the last tile to finish
 // merges every tile's partial result.
 constexpr int kTileRows = 64;
+// Fixed words at the start of a draft-head workspace (byte offsets). The
+// status words are described with vt_draft_head_status in vocabtrim.h.
+constexpr size_t kWsTicket = 0;     // uint32 ticket counter, zero between calls
+constexpr size_t kWsMerged = 64;    // uint32 finished row mergers, zero between calls
+constexpr size_t kWsError = VT_WS_ERROR_OFFSET;        // uint32 sticky error word
+constexpr size_t kWsHold = VT_WS_HOLD_OFFSET;          // uint32, see vocabtrim.h
+constexpr size_t kWsSpinLimit = VT_WS_SPIN_LIMIT_OFFSET;  // uint32, see vocabtrim.h
 struct HeadPlan {
   int32_t tiles;
   size_t off_group, zero_bytes, off_tile_keys, off_tile_ms, off_tile_z, off_hpack, off_zbuf;
   size_t bytes;
 };
 HeadPlan head_plan(int32_t M, int32_t V_high, int32_t k);
+// Bytes at the start of every draft-head workspace that must be zero before
+// the first call (every call leaves them so).
+size_t head_zero_bytes();
+// Zero-fills n bytes (n a multiple of 16) on the stream with a kernel.
+hipError_t launch_zero(void *p, size_t n, hipStream_t stream);
 // bias: bf16[V_high] added to the logits, or nullptr for a head without one.
+// remap: full ids through t2f (the method); false: trimmed indices j.
 hipError_t launch_draft_head(const uint16_t *h, int32_t M, int32_t d,
                              const uint16_t *W_trim, const uint16_t *bias, int32_t V_high,
                              const int32_t *t2f, int32_t k, int32_t *full_ids,
-                             float *probs, void *ws, hipStream_t stream);
+                             float *probs, void *ws, hipStream_t stream, bool remap = true);
 hipError_t launch_draft_sample(const uint16_t *h, int32_t M, int32_t d,
                                const uint16_t *W_trim, const uint16_t *bias, int32_t V_high,
                                const int32_t *t2f, uint64_t seed, uint64_t offset,
@@ -68,6 +82,10 @@ hipError_t launch_coverage(const uint32_t *counts, int32_t V, const int32_t *ord
 
 hipError_t launch_head_logits(const uint16_t *h, int32_t M, int32_t d,
                               const uint16_t *W_trim, int32_t V_high,
-                              float *logits, hipStream_t stream);
+                              float *logits, float *row_max, float *row_sum,
+                              hipStream_t stream);
+
+// Streaming read of a buffer (the draft head's practical ceiling).
+hipError_t launch_stream_read(const void *p, size_t bytes, uint64_t *sink, hipStream_t stream);
 
 }  // namespace vt

@@ -55,7 +55,8 @@ typedef enum {
     VT_ERR_INVALID_ARG = -1,  /* null/misaligned pointer or size out of range */
     VT_ERR_UNSUPPORTED = -2,  /* valid request beyond the library's limits   */
     VT_ERR_WORKSPACE = -3,    /* workspace missing, misaligned or too small   */
-    VT_ERR_HIP = -4           /* a HIP launch or query failed                 */
+    VT_ERR_HIP = -4,          /* a HIP launch or query failed                 */
+    VT_ERR_TIMEOUT = -5       /* a bounded wait inside a kernel gave up       */
 } vt_status;
 
 /* Static text for a status code (never NULL). */
@@ -180,9 +181,23 @@ int vt_gather_bias(const uint16_t *b, int32_t V, const int32_t *t2f, int32_t V_h
  *   the k largest z[m, j] in rank order (equal logits: lower full id first)
  *   full_ids[m, r] = t2f[j_r],   probs[m, r] = exp(z[m, j_r] - mu) / S
  * The pick is a deterministic top-k; probs are subset-softmax values (not
- * renormalised over the k picks); temperature is 1. The logits never leave
- * the chip: one kernel streams W_trim once and merges per-tile partial
- * results in a fixed order, so repeated calls give identical bits.
+ * renormalised over the k picks); temperature is 1. Partial results of
+ * tiles of 64 kept rows are merged in a fixed order, so repeated calls give
+ * identical bits.
+ *
+ * What runs, by number of draft rows (W_trim is read from memory once in
+ * every case):
+ *   M <= 2      one kernel: a GEMV over W_trim whose workgroups rank each
+ *               tile's logits on chip and publish per tile only the softmax
+ *               partial and the tile's top-k keys; the last workgroups to
+ *               finish merge them. No logit is written to memory.
+ *   3 <= M <= 64   an MFMA skinny GEMM (one workgroup per tile; past 32 rows
+ *               a small kernel first re-lays h out in operand order), then one
+ *               merge workgroup per draft row. The fp32 logits of every tile
+ *               go to the workspace and the merge reads back those of the
+ *               few tiles that can hold a pick.
+ *   M > 64      a GEMM-tiled MFMA kernel (128 x 128 blocks), logits to the
+ *               workspace, then the same per-row merge.
  *
  * h         device, bf16[M, d], 16-byte aligned; 1 <= M <= VT_M_MAX
  * d         d % 8 == 0, 8 <= d <= VT_D_MAX
@@ -195,7 +210,14 @@ int vt_gather_bias(const uint16_t *b, int32_t V, const int32_t *t2f, int32_t V_h
  * full_ids  device, int32[M, k];  probs  device, float[M, k]
  * ws        device workspace of vt_draft_head_workspace_size(M, V_high, d, k)
  *           bytes, 256-byte aligned. It must be zero-filled once before its
- *           first use; every call leaves its counters at zero again. */
+ *           first use; every call leaves its counters at zero again. Its
+ *           first 256 bytes hold the library's counters and status words
+ *           (see vt_draft_head_status).
+ * A merging workgroup waits, boundedly, for the other workgroups to arrive
+ * (only with two draft rows). If that wait gives up (another process kept
+ * workgroups from running for tens of milliseconds), the affected rows get
+ * full_ids = -1 and NaN probabilities, and the workspace's error word is
+ * raised; vt_draft_head_status reports and clears it. */
 size_t vt_draft_head_workspace_size(int32_t M, int32_t V_high, int32_t d,
                                     int32_t k);
 int vt_draft_head(const uint16_t *h, int32_t M, int32_t d,
@@ -248,14 +270,58 @@ int vt_draft_sample_bias(const uint16_t *h, int32_t M, int32_t d,
                          int32_t *full_ids, float *probs, void *ws, size_t ws_bytes,
                          void *stream);
 
+/* Status of the kernels that last used a draft-head workspace. Waits on the
+ * stream (host-blocking: not for use under graph capture), then returns
+ * VT_ERR_TIMEOUT if a bounded wait inside a kernel gave up since the last
+ * query (the affected outputs hold -1 / NaN) and clears the word, else
+ * VT_OK. ws: a draft-head workspace, or NULL for the library's own scratch
+ * on the current device (vt_draft_head_noalloc).
+ *
+ * Workspace words (byte offsets; all zero in normal use):
+ *   VT_WS_ERROR_OFFSET       uint32, set to 1 when a bounded wait gives up.
+ *   VT_WS_HOLD_OFFSET        uint32, for tests of the timeout path: the
+ *                            merging workgroups wait for this many extra
+ *                            arrivals that never come, so their wait gives
+ *                            up while every kernel still ends normally.
+ *   VT_WS_SPIN_LIMIT_OFFSET  uint32, when nonzero it replaces the wait's
+ *                            bound (in sleeps of about 128 clocks), so that
+ *                            such a test ends quickly. */
+#define VT_WS_ERROR_OFFSET 128
+#define VT_WS_HOLD_OFFSET 132
+#define VT_WS_SPIN_LIMIT_OFFSET 136
+int vt_draft_head_status(const void *ws, void *stream);
+
 /* ------------------------------------------------------- logits (checks)
  * The trimmed logits alone, z[m, j] as defined for vt_draft_head, written to
- * logits (device, float[M, V_high]). For parity diagnostics: it writes the
- * M x V_high logits to memory, which vt_draft_head never does.
+ * logits (device, float[M, V_high]), and the subset softmax statistics of
+ * each row from those fp32 logits: row_max[m] = max_j z[m, j] and
+ * row_sum[m] = sum_j exp(z[m, j] - row_max[m]) (device, float[M] each, or
+ * NULL to skip). For parity diagnostics: it writes the M x V_high logits to
+ * memory, which the draft head avoids.
  * Same argument rules as vt_draft_head. */
 int vt_head_logits(const uint16_t *h, int32_t M, int32_t d,
                    const uint16_t *W_trim, int32_t V_high, float *logits,
-                   void *stream);
+                   float *row_max, float *row_sum, void *stream);
+
+/* ------------------------------------------------------- remap cost (checks)
+ * vt_draft_head without the remap: the picks are returned as trimmed
+ * indices j (so equal logits rank by lower j) and t2f is not read. The
+ * VocabTrim page's guidance table puts the cost of mapping trimmed ids back
+ * to full ids below 1 %; comparing this call with vt_draft_head measures it.
+ * Arguments as for vt_draft_head, with t2f absent and trimmed_ids in place of
+ * full_ids (device, int32[M, k]). */
+int vt_draft_head_trimmed(const uint16_t *h, int32_t M, int32_t d,
+                          const uint16_t *W_trim, int32_t V_high, int32_t k,
+                          int32_t *trimmed_ids, float *probs, void *ws,
+                          size_t ws_bytes, void *stream);
+
+/* ----------------------------------------------------- streaming ceiling
+ * A plain read of `bytes` bytes of device memory with the draft head's load
+ * width and cache policy (16-byte non-temporal loads, one pass), folding
+ * the data into one word written to *sink (device uint64). It does no other
+ * work, so its time is the practical ceiling of the draft head, which reads
+ * W_trim once. p and bytes must be 16-byte aligned / a multiple of 16. */
+int vt_stream_read(const void *p, size_t bytes, uint64_t *sink, void *stream);
 
 #ifdef __cplusplus
 }

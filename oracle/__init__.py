@@ -61,6 +61,8 @@ def _load():
             lib.or_gumbel_block.restype = C.c_int
             lib.or_coverage_curve.argtypes = [P, i32, P, i32, C.c_double, P, P, P]
             lib.or_threads.argtypes = []
+            lib.or_set_threads.argtypes = [C.c_int]
+            lib.or_set_threads.restype = C.c_int
             for f in (lib.or_threads, lib.or_count, lib.or_select, lib.or_gather, lib.or_logits,
                       lib.or_softmax, lib.or_topk, lib.or_draft_head, lib.or_draft_sample,
                       lib.or_coverage_curve):
@@ -72,6 +74,12 @@ def _load():
 def threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return int(_load().or_threads())
+
+
+def set_threads(n: int) -> int:
+    """Sets the OpenMP thread count of later calls (results do not depend on
+    it); returns the count now in effect."""
+    return int(_load().or_set_threads(int(n)))
 
 
 def _p(a: np.ndarray | None):

@@ -31,7 +31,8 @@
  *   - the page's multinomial draw (or_draft_sample) is a Gumbel-max draw
  *     whose uniforms come from the counter-based generator Philox4x32-10
  *     (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as
- *     1, 2, 3", SC 2011), one generator call per (row, trimmed index).
+ *     1, 2, 3", SC 2011); one generator call per (block of four rows,
+ *     trimmed index) gives the four rows' uniforms, one output word each.
  *
  * Parity pins: every function here is pinned by the CPU tests against
  * library routines, closed forms, brute force or hand-worked examples.
@@ -67,6 +68,19 @@ int or_threads(void)
 #else
     return 1;
 #endif
+}
+
+/* Sets the number of threads of later OpenMP loops (results do not depend
+ * on it); returns the number now in effect. */
+int or_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+    return or_threads();
 }
 
 /* Step 1 of [VT] (count every sampled token id) and [FR]'s corpus frequency

@@ -142,10 +142,35 @@ def test_draft_head_validation(lib):
 
 def test_head_logits_validation(lib):
     f = lib.vt_head_logits
-    assert f(A, 1, 4096, A, 32768, None, None) == INVALID
-    assert f(A, 0, 4096, A, 32768, A, None) == INVALID
-    assert f(A, 1, 4095, A, 32768, A, None) == INVALID
-    assert f(A, 513, 4096, A, 32768, A, None) == UNSUPPORTED
+    assert f(A, 1, 4096, A, 32768, None, None, None, None) == INVALID
+    assert f(A, 1, 4096, A, 32768, None, A, A, None) == INVALID
+    assert f(A, 0, 4096, A, 32768, A, None, None, None) == INVALID
+    assert f(A, 1, 4095, A, 32768, A, None, None, None) == INVALID
+    assert f(A, 513, 4096, A, 32768, A, A, A, None) == UNSUPPORTED
+
+
+def test_draft_head_trimmed_validation(lib):
+    n = lib.vt_draft_head_workspace_size(1, 32768, 4096, 10)
+    f = lib.vt_draft_head_trimmed
+    assert f(None, 1, 4096, A, 32768, 10, A, A, A, n, None) == INVALID
+    assert f(A, 1, 4096, A, 32768, 10, None, A, A, n, None) == INVALID
+    assert f(A, 1, 4096, A, 32768, 10, A, None, A, n, None) == INVALID
+    assert f(A, 1, 4096, A, 32768, 0, A, A, A, n, None) == INVALID
+    assert f(A, 1, 4096, A, 32768, 65, A, A, A, n, None) == UNSUPPORTED
+    assert f(A, 1, 4096, A, 5, 6, A, A, A, n, None) == INVALID
+    assert f(A, 1, 4096, A, 32768, 10, A, A, None, n, None) == WORKSPACE
+    assert f(A, 1, 4096, A, 32768, 10, A, A, A, n - 1, None) == WORKSPACE
+
+
+def test_status_and_stream_read_validation(lib):
+    assert lib.vt_draft_head_status(None, None) == INVALID
+    f = lib.vt_stream_read
+    assert f(None, 1024, A, None) == INVALID
+    assert f(A, 1024, None, None) == INVALID
+    assert f(A, 0, A, None) == INVALID
+    assert f(A, 1000, A, None) == INVALID                              # not a multiple of 16
+    assert f(A + 8, 1024, A, None) == INVALID                           # misaligned
+    assert lib.vt_status_string(-5) != lib.vt_status_string(-4)
 
 
 def test_binding_fails_loudly_without_gpu_tensors():
