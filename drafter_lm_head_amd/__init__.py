@@ -15,6 +15,8 @@ stream. The functions keep the C names:
   with ``stats=True`` also (row_max f32[M], row_sum f32[M])
 * ``vt_draft_head_trimmed(h, W_trim, k)`` -> (trimmed_ids, probs): the draft
   step without the remap (measures the remap's cost)
+* ``vt_draft_head_noalloc(h, W_trim, t2f, k)``: vt_draft_head on the
+  library's fixed per-GPU scratch (no workspace, no device allocation inside)
 * ``vt_draft_head_status(ws)``         -> raises VtError if a bounded wait in a
   kernel gave up since the last query (host-blocking)
 * ``vt_stream_read(buf)``              : a plain streaming read of a buffer
@@ -41,6 +43,7 @@ __all__ = [
     "vt_select_vocab_workspace_size", "vt_draft_head_workspace_size",
     "coverage", "vt_coverage_curve", "vt_coverage_curve_workspace_size",
     "vt_draft_head_trimmed", "vt_draft_head_status", "vt_stream_read",
+    "vt_draft_head_noalloc", "VT_NOALLOC_WS_BYTES", "VT_ERR_SCRATCH_LIMIT",
     "VT_WS_ERROR_OFFSET", "VT_WS_HOLD_OFFSET", "VT_WS_SPIN_LIMIT_OFFSET",
 ]
 
@@ -48,7 +51,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libvocabtrim.so")
 
 VT_OK, VT_ERR_INVALID_ARG, VT_ERR_UNSUPPORTED, VT_ERR_WORKSPACE, VT_ERR_HIP = 0, -1, -2, -3, -4
-VT_ERR_TIMEOUT = -5
+VT_ERR_TIMEOUT, VT_ERR_SCRATCH_LIMIT = -5, -6
+VT_NOALLOC_WS_BYTES = 16 << 20
 VT_K_MAX, VT_M_MAX, VT_D_MAX, VT_VHIGH_MAX = 64, 512, 8192, 262144
 VT_WS_ERROR_OFFSET, VT_WS_HOLD_OFFSET, VT_WS_SPIN_LIMIT_OFFSET = 128, 132, 136
 
@@ -74,6 +78,7 @@ _SIGS = {
     "vt_head_logits": (_INT, [_P, _I32, _I32, _P, _I32, _P, _P, _P, _P]),
     "vt_draft_head_trimmed": (_INT, [_P, _I32, _I32, _P, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "vt_draft_head_status": (_INT, [_P, _P]),
+    "vt_draft_head_noalloc": (_INT, [_P, _I32, _I32, _P, _I32, _P, _I32, _P, _P, _P]),
     "vt_stream_read": (_INT, [_P, _SZ, _P, _P]),
     "vt_coverage_curve_workspace_size": (_SZ, [_I32, _I32]),
     "vt_coverage_curve": (_INT, [_P, _I32, _P, _I32, C.c_double, _P, _P, _P, _P, _SZ, _P]),
@@ -401,10 +406,39 @@ def vt_draft_head_trimmed(h: torch.Tensor, W_trim: torch.Tensor, k: int,
     return trimmed_ids, probs
 
 
-def vt_draft_head_status(ws: torch.Tensor) -> None:
+def vt_draft_head_noalloc(h: torch.Tensor, W_trim: torch.Tensor, t2f: torch.Tensor, k: int,
+                          full_ids: torch.Tensor | None = None,
+                          probs: torch.Tensor | None = None):
+    """vt_draft_head on the library's fixed per-GPU scratch: the C call takes
+    no workspace and allocates nothing (pass ``full_ids`` and ``probs`` to
+    allocate nothing here either, e.g. under graph capture)."""
+    M, d, V_high = _head_shapes(h, W_trim, t2f, None)
+    dev = h.device
+    if full_ids is None:
+        full_ids = torch.empty((M, k), dtype=torch.int32, device=dev)
+    if probs is None:
+        probs = torch.empty((M, k), dtype=torch.float32, device=dev)
+    _dev(full_ids, "full_ids", (torch.int32,))
+    _dev(probs, "probs", (torch.float32,))
+    if full_ids.numel() != M * k or probs.numel() != M * k:
+        raise ValueError("outputs must hold M * k entries")
+    _check(lib().vt_draft_head_noalloc(_ptr(h), M, d, _ptr(W_trim), V_high, _ptr(t2f), k,
+                                       _ptr(full_ids), _ptr(probs), _stream(h)),
+           "vt_draft_head_noalloc")
+    return full_ids, probs
+
+
+def vt_draft_head_status(ws: torch.Tensor | None, device: torch.device | None = None) -> None:
     """Raises VtError(VT_ERR_TIMEOUT) if a bounded wait inside a kernel that
-    used this draft-head workspace gave up since the last query (clearing
-    the flag). Blocks the host until the stream's work is done."""
+    used this draft-head workspace (None: the library's own scratch of
+    vt_draft_head_noalloc on ``device``) gave up since the last query,
+    clearing the flag. Blocks the host until the stream's work is done."""
+    if ws is None:
+        dev = torch.device(device if device is not None else "cuda")
+        with torch.cuda.device(dev):
+            st = lib().vt_draft_head_status(None, torch.cuda.current_stream(dev).cuda_stream)
+        _check(st, "vt_draft_head_status")
+        return
     _dev(ws, "ws", (torch.uint8,), 1)
     _check(lib().vt_draft_head_status(_ptr(ws), _stream(ws)), "vt_draft_head_status")
 

@@ -5,6 +5,8 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 #include "vt_internal.hpp"
 
 namespace {
@@ -28,6 +30,38 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// Scratch of vt_draft_head_noalloc: a fixed array in device memory, one
+// copy per GPU (each device that loads the library holds it until the
+// process ends). Host code never passes the array's name to a kernel: its
+// device address is taken once per device with hipGetSymbolAddress and kept
+// in g_scratch.
+static __device__ __align__(256) unsigned char scratch[VT_NOALLOC_WS_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];  // device address of `scratch` per device, once set up
+
+// The current device's scratch address. On the first call on a device it
+// takes the address and clears the counters at its start (a fill kernel on
+// `stream`, ahead of the caller's kernels). Returns a vt_status.
+int device_scratch(bool set_up, hipStream_t stream, void **out) {
+  *out = nullptr;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hip_status(hipErrorInvalidDevice);
+  if (dev < 0 || dev >= kMaxDevices) return VT_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev] && set_up) {
+    void *p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_status(e == hipSuccess ? hipErrorInvalidSymbol : e);
+    e = vt::launch_zero(p, vt::head_zero_bytes(), stream);
+    if (e != hipSuccess) return hip_status(e);
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return VT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -40,6 +74,8 @@ const char *vt_status_string(int status) {
     case VT_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case VT_ERR_HIP: return "HIP launch failed";
     case VT_ERR_TIMEOUT: return "a bounded wait inside a kernel gave up (outputs hold -1 / NaN)";
+    case VT_ERR_SCRATCH_LIMIT:
+      return "request needs more scratch than the library's fixed scratch (VT_NOALLOC_WS_BYTES)";
     default: return "unknown status";
   }
 }
@@ -204,6 +240,23 @@ int vt_draft_sample_bias(const uint16_t *h, int32_t M, int32_t d,
                                             full_ids, probs, ws, as_stream(stream)));
 }
 
+int vt_draft_head_noalloc(const uint16_t *h, int32_t M, int32_t d,
+                          const uint16_t *W_trim, int32_t V_high, const int32_t *t2f,
+                          int32_t k, int32_t *full_ids, float *probs, void *stream) {
+  int st = check_head(h, M, d, W_trim, V_high);
+  if (st != VT_OK) return st;
+  if (!t2f || !full_ids || !probs) return VT_ERR_INVALID_ARG;
+  if (k <= 0 || k > V_high) return VT_ERR_INVALID_ARG;
+  if (k > VT_K_MAX) return VT_ERR_UNSUPPORTED;
+  if (vt_draft_head_workspace_size(M, V_high, d, k) > (size_t)VT_NOALLOC_WS_BYTES)
+    return VT_ERR_SCRATCH_LIMIT;
+  void *ws = nullptr;
+  st = device_scratch(true, as_stream(stream), &ws);
+  if (st != VT_OK) return st;
+  return hip_status(vt::launch_draft_head(h, M, d, W_trim, nullptr, V_high, t2f, k, full_ids,
+                                          probs, ws, as_stream(stream)));
+}
+
 int vt_draft_head_trimmed(const uint16_t *h, int32_t M, int32_t d,
                           const uint16_t *W_trim, int32_t V_high, int32_t k,
                           int32_t *trimmed_ids, float *probs, void *ws,
@@ -222,8 +275,14 @@ int vt_draft_head_trimmed(const uint16_t *h, int32_t M, int32_t d,
 }
 
 int vt_draft_head_status(const void *ws, void *stream) {
-  if (!ws) return VT_ERR_INVALID_ARG;
   const hipStream_t s = as_stream(stream);
+  if (!ws) {  // the library's own scratch on the current device
+    void *p = nullptr;
+    const int st = device_scratch(false, s, &p);
+    if (st != VT_OK) return st;
+    if (!p) return VT_OK;  // never used on this device
+    ws = p;
+  }
   char *word = static_cast<char *>(const_cast<void *>(ws)) + VT_WS_ERROR_OFFSET;
   uint32_t v = 0;
   if (hipMemcpyAsync(&v, word, sizeof v, hipMemcpyDeviceToHost, s) != hipSuccess ||

@@ -56,7 +56,9 @@ typedef enum {
     VT_ERR_UNSUPPORTED = -2,  /* valid request beyond the library's limits   */
     VT_ERR_WORKSPACE = -3,    /* workspace missing, misaligned or too small   */
     VT_ERR_HIP = -4,          /* a HIP launch or query failed                 */
-    VT_ERR_TIMEOUT = -5       /* a bounded wait inside a kernel gave up       */
+    VT_ERR_TIMEOUT = -5,      /* a bounded wait inside a kernel gave up       */
+    VT_ERR_SCRATCH_LIMIT = -6 /* vt_draft_head_noalloc: request exceeds the
+                                 library's fixed scratch                      */
 } vt_status;
 
 /* Static text for a status code (never NULL). */
@@ -225,6 +227,24 @@ int vt_draft_head(const uint16_t *h, int32_t M, int32_t d,
                   int32_t k, int32_t *full_ids, float *probs, void *ws,
                   size_t ws_bytes, void *stream);
 
+/* vt_draft_head for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It takes no workspace: its scratch is a fixed array of
+ * VT_NOALLOC_WS_BYTES inside the library, one per GPU, held until the
+ * process ends. The call allocates nothing (the first call on a device
+ * takes the array's address and clears its counters with a kernel on
+ * `stream`; do not make that first call under graph capture). Every call on
+ * a GPU shares that GPU's array: calls that overlap on one GPU (different
+ * streams, threads or processes without stream order) race and give wrong
+ * results. Requests whose vt_draft_head_workspace_size exceeds
+ * VT_NOALLOC_WS_BYTES return VT_ERR_SCRATCH_LIMIT and launch nothing.
+ * Results are those of vt_draft_head. vt_draft_head_status(NULL, stream)
+ * reports on this scratch. Other arguments as for vt_draft_head. */
+#define VT_NOALLOC_WS_BYTES (16u << 20)
+int vt_draft_head_noalloc(const uint16_t *h, int32_t M, int32_t d,
+                          const uint16_t *W_trim, int32_t V_high, const int32_t *t2f,
+                          int32_t k, int32_t *full_ids, float *probs, void *stream);
+
 /* vt_draft_head for a trimmed head with a bias ([VT] Step 3 keeps the bias
  * of the kept ids; the trimmed head is a linear layer with that bias):
  *   z[m, j] = sum_t h[m, t] * W_trim[j, t] + bias[j]   (fp32)
@@ -275,7 +295,7 @@ int vt_draft_sample_bias(const uint16_t *h, int32_t M, int32_t d,
  * VT_ERR_TIMEOUT if a bounded wait inside a kernel gave up since the last
  * query (the affected outputs hold -1 / NaN) and clears the word, else
  * VT_OK. ws: a draft-head workspace, or NULL for the library's own scratch
- * on the current device (vt_draft_head_noalloc).
+ * on the current device (vt_draft_head_noalloc; VT_OK if never used).
  *
  * Workspace words (byte offsets; all zero in normal use):
  *   VT_WS_ERROR_OFFSET       uint32, set to 1 when a bounded wait gives up.

@@ -162,8 +162,22 @@ def test_draft_head_trimmed_validation(lib):
     assert f(A, 1, 4096, A, 32768, 10, A, A, A, n - 1, None) == WORKSPACE
 
 
+def test_noalloc_validation(lib):
+    f = lib.vt_draft_head_noalloc
+    assert f(None, 1, 4096, A, 32768, A, 10, A, A, None) == INVALID
+    assert f(A, 1, 4096, A, 32768, None, 10, A, A, None) == INVALID
+    assert f(A, 1, 4096, A, 32768, A, 10, None, A, None) == INVALID
+    assert f(A, 1, 4096, A, 32768, A, 10, A, None, None) == INVALID
+    assert f(A, 1, 4096, A, 32768, A, 0, A, A, None) == INVALID
+    assert f(A, 1, 4096, A, 32768, A, 65, A, A, None) == UNSUPPORTED
+    assert f(A, 513, 4096, A, 32768, A, 10, A, A, None) == UNSUPPORTED
+    # beyond the fixed scratch: refused before any HIP call
+    assert lib.vt_draft_head_workspace_size(512, 262144, 64, 10) > (16 << 20)
+    assert f(A, 512, 64, A, 262144, A, 10, A, A, None) == -6
+    assert lib.vt_status_string(-6) != lib.vt_status_string(-2)
+
+
 def test_status_and_stream_read_validation(lib):
-    assert lib.vt_draft_head_status(None, None) == INVALID
     f = lib.vt_stream_read
     assert f(None, 1024, A, None) == INVALID
     assert f(A, 1024, None, None) == INVALID
