@@ -37,7 +37,7 @@ import torch
 
 __all__ = [
     "VtError", "lib", "lib_path", "VT_K_MAX", "VT_M_MAX", "VT_D_MAX",
-    "VT_VHIGH_MAX", "vt_count_freq", "vt_select_vocab", "vt_gather_head",
+    "VT_VHIGH_MAX", "VT_V_MAX", "vt_count_freq", "vt_select_vocab", "vt_gather_head",
     "vt_draft_head", "vt_draft_sample", "vt_head_logits", "vt_count_freq_workspace_size",
     "vt_gather_bias", "vt_draft_head_bias", "vt_draft_sample_bias",
     "vt_select_vocab_workspace_size", "vt_draft_head_workspace_size",
@@ -53,7 +53,7 @@ lib_path = os.path.join(_HERE, "libvocabtrim.so")
 VT_OK, VT_ERR_INVALID_ARG, VT_ERR_UNSUPPORTED, VT_ERR_WORKSPACE, VT_ERR_HIP = 0, -1, -2, -3, -4
 VT_ERR_TIMEOUT, VT_ERR_SCRATCH_LIMIT = -5, -6
 VT_NOALLOC_WS_BYTES = 16 << 20
-VT_K_MAX, VT_M_MAX, VT_D_MAX, VT_VHIGH_MAX = 64, 512, 8192, 262144
+VT_K_MAX, VT_M_MAX, VT_D_MAX, VT_VHIGH_MAX, VT_V_MAX = 64, 512, 8192, 262144, 1 << 26
 VT_WS_ERROR_OFFSET, VT_WS_HOLD_OFFSET, VT_WS_SPIN_LIMIT_OFFSET = 128, 132, 136
 
 _lock = threading.Lock()

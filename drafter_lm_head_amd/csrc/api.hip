@@ -84,7 +84,7 @@ int vt_version(void) { return VT_ABI_VERSION; }
 
 // ------------------------------------------------------------------ count
 size_t vt_count_freq_workspace_size(uint64_t n, int32_t V) {
-  if (V <= 0) return 0;
+  if (V <= 0 || V > VT_V_MAX) return 0;
   const vt::CountPlan p = vt::count_plan(n, V);
   return p.partial_bytes + p.inv_bytes + p.spill_bytes;
 }
@@ -94,6 +94,7 @@ int vt_count_freq(const int32_t *ids, uint64_t n, int32_t V, uint32_t *counts,
                   size_t ws_bytes, void *stream) {
   if (V <= 0 || n > UINT32_MAX || !counts || !n_invalid) return VT_ERR_INVALID_ARG;
   if (n > 0 && (!ids || !aligned(ids, 16))) return VT_ERR_INVALID_ARG;
+  if (V > VT_V_MAX) return VT_ERR_UNSUPPORTED;
   if (!ws || !aligned(ws, 256) || ws_bytes < vt_count_freq_workspace_size(n, V))
     return VT_ERR_WORKSPACE;
   return hip_status(vt::launch_count(ids, n, V, counts, accumulate ? 1 : 0,
@@ -102,7 +103,7 @@ int vt_count_freq(const int32_t *ids, uint64_t n, int32_t V, uint32_t *counts,
 
 // ----------------------------------------------------------------- select
 size_t vt_select_vocab_workspace_size(int32_t V, int32_t V_high) {
-  if (V <= 0 || V_high <= 0 || V_high > V) return 0;
+  if (V <= 0 || V_high <= 0 || V_high > V || V > VT_V_MAX) return 0;
   return vt::select_ws_bytes(V, V_high);
 }
 
@@ -113,6 +114,7 @@ int vt_select_vocab(const uint32_t *counts, int32_t V, int32_t V_high,
   if (!counts || !t2f || !sel_sum || !tot_sum) return VT_ERR_INVALID_ARG;
   if (!aligned(counts, 16)) return VT_ERR_INVALID_ARG;
   if (V <= 0 || V_high <= 0 || V_high > V) return VT_ERR_INVALID_ARG;
+  if (V > VT_V_MAX) return VT_ERR_UNSUPPORTED;
   if (!ws || !aligned(ws, 256) ||
       ws_bytes < vt_select_vocab_workspace_size(V, V_high))
     return VT_ERR_WORKSPACE;
@@ -122,7 +124,7 @@ int vt_select_vocab(const uint32_t *counts, int32_t V, int32_t V_high,
 
 // --------------------------------------------------------- coverage curve
 size_t vt_coverage_curve_workspace_size(int32_t V, int32_t L) {
-  if (V <= 0 || L <= 0 || L > V) return 0;
+  if (V <= 0 || L <= 0 || L > V || V > VT_V_MAX) return 0;
   return vt::coverage_ws_bytes(V, L);
 }
 
@@ -132,6 +134,7 @@ int vt_coverage_curve(const uint32_t *counts, int32_t V, const int32_t *order,
                       size_t ws_bytes, void *stream) {
   if (!counts || !order || !cum || !tot_sum) return VT_ERR_INVALID_ARG;
   if (V <= 0 || L <= 0 || L > V) return VT_ERR_INVALID_ARG;
+  if (V > VT_V_MAX) return VT_ERR_UNSUPPORTED;
   if (!ws || !aligned(ws, 256) || ws_bytes < vt_coverage_curve_workspace_size(V, L))
     return VT_ERR_WORKSPACE;
   return hip_status(vt::launch_coverage(counts, V, order, L, min_coverage, cum,
@@ -145,6 +148,7 @@ int vt_gather_head(const uint16_t *W, int32_t V, int32_t d,
   if (!W || !t2f || !W_trim) return VT_ERR_INVALID_ARG;
   if (V <= 0 || V_high <= 0 || !valid_d(d)) return VT_ERR_INVALID_ARG;
   if (!aligned(W, 16) || !aligned(W_trim, 16)) return VT_ERR_INVALID_ARG;
+  if (V > VT_V_MAX || V_high > VT_V_MAX) return VT_ERR_UNSUPPORTED;
   if (overlaps(W, (size_t)V * d * 2, W_trim, (size_t)V_high * d * 2))
     return VT_ERR_INVALID_ARG;
   return hip_status(vt::launch_gather(W, V, d, t2f, V_high, W_trim, n_bad,
@@ -155,6 +159,7 @@ int vt_gather_bias(const uint16_t *b, int32_t V, const int32_t *t2f, int32_t V_h
                    uint16_t *b_trim, uint32_t *n_bad, void *stream) {
   if (!b || !t2f || !b_trim) return VT_ERR_INVALID_ARG;
   if (V <= 0 || V_high <= 0) return VT_ERR_INVALID_ARG;
+  if (V > VT_V_MAX || V_high > VT_V_MAX) return VT_ERR_UNSUPPORTED;
   if (overlaps(b, (size_t)V * 2, b_trim, (size_t)V_high * 2)) return VT_ERR_INVALID_ARG;
   return hip_status(vt::launch_gather_bias(b, V, t2f, V_high, b_trim, n_bad,
                                            as_stream(stream)));

@@ -49,6 +49,8 @@ extern "C" {
 #define VT_M_MAX 512          /* draft rows per vt_draft_head call           */
 #define VT_D_MAX 8192         /* hidden size; d must also be a multiple of 8 */
 #define VT_VHIGH_MAX 262144   /* kept vocabulary per vt_draft_head call     */
+#define VT_V_MAX (1 << 26)    /* full vocabulary of the count, select,
+                                 coverage and gather calls               */
 
 typedef enum {
     VT_OK = 0,
@@ -76,7 +78,7 @@ int vt_version(void);
  *
  * ids       device, int32[n], 16-byte aligned (may be NULL when n == 0)
  * n         number of ids, n <= UINT32_MAX
- * V         full vocabulary, 1 <= V < 2^31
+ * V         full vocabulary, 1 <= V <= VT_V_MAX (larger: VT_ERR_UNSUPPORTED)
  * counts    device, uint32[V]; overwritten, or added to when accumulate != 0
  * n_invalid device, uint64[1]; overwritten, or added to when accumulate != 0
  * ws        device workspace of at least vt_count_freq_workspace_size(n, V)
@@ -103,7 +105,7 @@ int vt_count_freq(const int32_t *ids, uint64_t n, int32_t V, uint32_t *counts,
  * id was counted).
  *
  * counts  device, uint32[V], 16-byte aligned
- * V, V_high  1 <= V_high <= V < 2^31
+ * V, V_high  1 <= V_high <= V <= VT_V_MAX (larger V: VT_ERR_UNSUPPORTED)
  * t2f     device, int32[V_high]
  * f2t     device, int32[V], or NULL to skip it
  * sel_sum, tot_sum  device, uint64[1] each
@@ -130,8 +132,9 @@ int vt_select_vocab(const uint32_t *counts, int32_t V, int32_t V_high,
  *             (double)tot_sum, or -1 if none (e.g. min_coverage > 1)
  * Coverage at n is cum[n - 1] / tot_sum (tot_sum == 0: no token counted).
  *
- * counts  device, uint32[V];  order  device, int32[L], 1 <= L <= V, e.g. the
- *         t2f of vt_select_vocab with V_high = L
+ * counts  device, uint32[V], V <= VT_V_MAX (larger: VT_ERR_UNSUPPORTED)
+ * order   device, int32[L], 1 <= L <= V, e.g. the t2f of vt_select_vocab
+ *         with V_high = L
  * cum     device, uint64[L];  tot_sum  device, uint64[1]
  * v_high  device, int32[1], or NULL to skip it
  * ws      device workspace of vt_coverage_curve_workspace_size(V, L) bytes,
@@ -150,6 +153,7 @@ int vt_coverage_curve(const uint32_t *counts, int32_t V, const int32_t *order,
  *   W_trim[i, :] = W[t2f[i], :]   for i < V_high  (bit copy)
  *
  * W       device, bf16[V, d], 16-byte aligned;  d % 8 == 0, 8 <= d <= VT_D_MAX
+ * V, V_high  at most VT_V_MAX each (larger: VT_ERR_UNSUPPORTED)
  * t2f     device, int32[V_high] (from vt_select_vocab or the caller)
  * W_trim  device, bf16[V_high, d], 16-byte aligned; must not overlap W
  * n_bad   device uint32[1] or NULL. A t2f entry outside [0, V) is not read

@@ -257,3 +257,19 @@ def test_bias_entry_points_validation(lib):
     assert sb(A, 3, 4096, A, A, 32768, None, 1, 2, A, A, A, n1, None) == INVALID
     assert sb(A, 3, 4096, A, A, 32768, A, 1, 2, A, A, None, n1, None) == WORKSPACE
     assert sb(A, 3, 4096, A, A, 32768, A, 1, 2, A, A, A, n1 - 1, None) == WORKSPACE
+
+
+def test_vocabulary_limit(lib):
+    # past VT_V_MAX ids the sizing functions give 0 and the calls refuse
+    import drafter_lm_head_amd as dlh
+    big = dlh.VT_V_MAX + 1
+    f = lib.vt_count_freq_workspace_size
+    assert f(1000, dlh.VT_V_MAX) > 0 and f(1000, big) == 0
+    assert lib.vt_select_vocab_workspace_size(big, 10) == 0
+    assert lib.vt_coverage_curve_workspace_size(big, 10) == 0
+    assert lib.vt_count_freq(A, 1000, big, A, 0, A, A, 1 << 40, None) == UNSUPPORTED
+    assert lib.vt_select_vocab(A, big, 10, A, A, A, A, A, 1 << 40, None) == UNSUPPORTED
+    assert lib.vt_coverage_curve(A, big, A, 10, C.c_double(0.9), A, A, A, A, 1 << 40,
+                                 None) == UNSUPPORTED
+    assert lib.vt_gather_head(A, big, 64, A, 10, A + (1 << 40), None, None) == UNSUPPORTED
+    assert lib.vt_gather_bias(A, big, A, 10, A + (1 << 40), None, None) == UNSUPPORTED
