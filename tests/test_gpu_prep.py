@@ -188,3 +188,29 @@ def test_prep_pipeline_llama(dlh):
     np.testing.assert_array_equal(f2t.cpu().numpy(), f2t_o)
     assert cov == sel_o / tot_o
     assert bf16_host(Wt).tobytes() == oracle.gather(W, t2f_o).tobytes()
+
+
+def test_mapping_saved_from_device_round_trips(dlh, tmp_path):
+    # The device's counts and maps, saved with their checksums and the
+    # stream's seed, load back bit for bit; the reloaded t2f gathers the same
+    # head as the device's own.
+    from drafter_lm_head_amd.mapping import load_mapping, save_mapping
+    rng = np.random.default_rng(23)
+    V, V_high, d = 128256, 32768, 64
+    ids = synth.zipf_ids(2_000_000, V, 1.1, rng)
+    c, _ = dlh.vt_count_freq(to_dev_i32(ids), V)
+    t2f, f2t, sel, tot = dlh.vt_select_vocab(c, V_high)
+    save_mapping(str(tmp_path), c, t2f, f2t, seed=23)
+    m = load_mapping(str(tmp_path))
+    np.testing.assert_array_equal(m.counts, u32_host(c))
+    np.testing.assert_array_equal(m.t2f, t2f.cpu().numpy())
+    np.testing.assert_array_equal(m.f2t, f2t.cpu().numpy())
+    assert m.sums() == (u64_scalar(sel), u64_scalar(tot)) and m.seed == 23
+    c_o, _ = oracle.count(ids, V)
+    np.testing.assert_array_equal(m.t2f, oracle.select(c_o, V_high)[0])
+    W = synth.head_weights(V, d, rng)
+    Wd = to_dev_bf16(W)
+    a = dlh.vt_gather_head(Wd, t2f)
+    b = dlh.vt_gather_head(Wd, to_dev_i32(m.t2f))
+    torch.cuda.synchronize()
+    assert bf16_host(a).tobytes() == bf16_host(b).tobytes()
