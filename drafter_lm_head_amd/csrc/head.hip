@@ -1,20 +1,27 @@
 // Frequency-ranked drafter head, one draft step (VocabTrim page,
-// Implementation, Step 4; FR-Spec notes, key design), for gfx950.
-//
-// One kernel streams W_trim[V_high, d] once and never writes the logits:
-//   * a workgroup owns a tile of kTileRows = 64 rows; each wave computes
-//     whole rows (16-byte coalesced loads over d, packed bf16 dot products
-//     with fp32 accumulation against h held in registers, then a DPP
-//     reduction across the wave);
-//   * the tile's logits go to LDS; per draft row one wave sorts the 64
-//     (logit, full id) keys, and writes the tile's top-k keys and its
-//     softmax partial (max, sum of exp(z - max)) to the workspace;
-//   * the workgroup that finishes last (atomic ticket) reads every tile's
-//     partial once and merges them: the online-softmax partials in a fixed
-//     order, the keys by a threshold filter and a sort, so results do not
-//     depend on scheduling; it writes full_ids and probs.
-// The kernel is bound by HBM bandwidth: it moves 2 * V_high * d bytes of
-// W_trim and does 2 * M * V_high * d flops.
+// Implementation, Step 4; FR-Spec notes, key design), for gfx950. Every path
+// reads W_trim[V_high, d] from memory once; they differ in what else they
+// write, by number of draft rows M:
+//   * M <= 2, one kernel (head_gemv_kernel), no logit written to memory:
+//     each wave computes whole rows (16-byte coalesced loads over d, packed
+//     bf16 dot products with fp32 accumulation against h held in
+//     registers, a DPP reduction); a tile's 64 logits go to LDS, where per
+//     draft row one wave ranks the (logit, full id) keys and publishes the
+//     tile's top-k keys and softmax partial (max, sum of exp(z - max)); the
+//     workgroup that finishes last (atomic ticket) reads every partial once
+//     and merges them: the softmax partials in a fixed order, the keys by a
+//     threshold filter and a rank, so results do not depend on scheduling.
+//   * 3 <= M <= 64: a skinny GEMM on the matrix cores (head_mfma_kernel; past
+//     32 rows h_pack_kernel first lays h out in operand order), which writes
+//     each tile's fp32 logits and softmax partials to the workspace, then one
+//     merge workgroup per draft row (tree_merge_kernel) that reads the
+//     partials and the logits of only the tiles that can hold a pick.
+//   * M > 64: a GEMM tiling of 128 x 128 blocks (head_gemm_kernel), then the
+//     same per-row merge.
+// Sampling (one draw per row) runs the same contraction kernels with a
+// per-tile draw in place of the logits. Up to M of about 312 the head is
+// bound by HBM bandwidth: it moves 2 * V_high * d bytes of W_trim for
+// 2 * M * V_high * d flops.
 #include <algorithm>
 
 #include "vt_internal.hpp"
