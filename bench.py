@@ -71,6 +71,24 @@ def per_launch_us(fn, n, torch):
     return 1000.0 * statistics.mean(a.elapsed_time(b) for a, b in evs)
 
 
+def host_call_us(fn, n, torch):
+    """Host wall-clock of the API call itself (argument checks, marshalling,
+    the kernel launches; no wait for the GPU), and of one call followed by a
+    device synchronisation (the latency a caller that needs the result at
+    once sees), each the median over n calls."""
+    call, sync = [], []
+    torch.cuda.synchronize()
+    for i in range(n):
+        a = time.perf_counter()
+        fn(i)
+        b = time.perf_counter()
+        torch.cuda.synchronize()
+        c = time.perf_counter()
+        call.append(b - a)
+        sync.append(c - a)
+    return 1e6 * statistics.median(call), 1e6 * statistics.median(sync)
+
+
 def median_us(fn, reps, torch):
     ts = []
     for _ in range(reps):
@@ -253,6 +271,7 @@ def main():
         return
     n_launch = min(args.steps, 1000)
     us_launch = per_launch_us(cold, n_launch, torch)
+    us_host_call, us_host_sync = host_call_us(cold, n_launch, torch)
     ms_warm = time_calls(warm, args.steps, torch) / args.steps
     log(f"warm: {ms_warm * 1000:.2f} us/step; single launches bracketed by events: {us_launch:.2f} us")
 
@@ -391,6 +410,11 @@ def main():
                           "(trimmed indices), interleaved, cold",
                   "us_with_remap": round(us_remap, 3), "us_without_remap": round(us_noremap, 3),
                   "overhead_frac": round((us_remap - us_noremap) / us_noremap, 5)},
+        "host": {"what": "host wall-clock per vt_draft_head call through the binding, launch "
+                         "included (median); and the same call followed by a device "
+                         "synchronisation",
+                 "us_per_api_call": round(us_host_call, 3),
+                 "us_call_to_result": round(us_host_sync, 3)},
         "graph": {"what": f"{n_graph} cold calls captured in one graph, replayed",
                   "us_per_call": round(us_graph, 3),
                   "GB_per_s": round(nb / (us_graph * 1e-6) / 1e9, 1)},

@@ -68,3 +68,40 @@ def test_noalloc_refuses_requests_beyond_its_scratch(dlh):
     assert e.value.status == dlh.VT_ERR_SCRATCH_LIMIT
     torch.cuda.synchronize()
     assert int((ids == -7).all().item()) == 1      # nothing was launched
+
+
+@pytest.mark.parametrize("M", [1, 60])
+def test_noalloc_graph_replays_match_eager(dlh, M):
+    # The caller it exists for: a captured serving loop. After a first eager
+    # call (which sets the scratch up), the call is captured in a HIP graph
+    # with preallocated outputs; every replay, with an unrelated eager call
+    # on the same scratch between some of them, gives the eager result.
+    V_high, d, k = 5000, 512, 10
+    h, W, t2f = case(300 + M, M, d, V_high, scale=2.0)
+    h2, _, _ = case(400 + M, M, d, V_high, scale=2.0)
+    ids = torch.empty((M, k), dtype=torch.int32, device=DEV)
+    probs = torch.empty((M, k), dtype=torch.float32, device=DEV)
+    run = lambda: dlh.vt_draft_head_noalloc(h, W, t2f, k, full_ids=ids, probs=probs)
+    run()
+    torch.cuda.synchronize()
+    ref = (host(ids).tobytes(), host(probs).tobytes())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    other_ids = torch.empty_like(ids)
+    other_probs = torch.empty_like(probs)
+    for rep in range(5):
+        ids.fill_(-1)
+        probs.fill_(-1.0)
+        if rep % 2:
+            dlh.vt_draft_head_noalloc(h2, W, t2f, k, full_ids=other_ids, probs=other_probs)
+        g.replay()
+        torch.cuda.synchronize()
+        assert (host(ids).tobytes(), host(probs).tobytes()) == ref, rep
+    dlh.vt_draft_head_status(None, DEV)
