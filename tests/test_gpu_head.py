@@ -72,10 +72,14 @@ def test_draft_tree_rows(dlh, M):
 @pytest.mark.parametrize("V_high,d,k,M", [(1, 256, 1, 60), (70, 520, 10, 60), (129, 8, 64, 60),
                                            (3000, 3584, 64, 60), (4097, 64, 10, 60),
                                            (8193, 128, 64, 60), (12288, 64, 33, 60),
-                                           (4097, 520, 33, 130), (65, 8, 64, 193)])
+                                           (4097, 520, 33, 130), (65, 8, 64, 193),
+                                           (777, 8192, 10, 64), (300, 8192, 16, 200),
+                                           (300, 8, 8, 40), (200, 8192, 10, 512)])
 def test_draft_tree_edges(dlh, V_high, d, k, M):
     # Ragged tiles and row groups: a last tile of one row, a last group of
-    # two (M = 130) or one (M = 193) draft rows.
+    # two (M = 130) or one (M = 193) draft rows; the longest rows (d = 8192)
+    # on the 64-row and GEMM-tiled kernels, and one 16-byte chunk per row
+    # (d = 8) with packed h.
     h, W, t2f = rand_case(300 + V_high, M, d, V_high, hscale=2.0)
     check_case(dlh, h, W, t2f, min(k, V_high))
 
