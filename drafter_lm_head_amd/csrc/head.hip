@@ -1209,14 +1209,29 @@ __global__ __launch_bounds__(WAVES *kWave) void tree_merge_kernel(HeadArgs a) {
 // row merges follow.
 // Against one 64 x 64 block per workgroup this halves the L2 traffic per
 // flop, which bounds the contraction at these sizes.
-constexpr int kGemmRows = 128;               // W rows and draft rows per workgroup
+constexpr int kGemmRows = 128;               // W rows per workgroup
 constexpr int kGemmKC = 8;                   // 16-byte chunks per row and K step
 constexpr int kGemmPitch = kGemmKC;          // staged row pitch in chunks (swizzled)
-constexpr int kGemmThreads = 4 * kWave;
 
+// A workgroup of 2 x WC waves covers 128 W rows and WC x 16 CB draft rows:
+// wave (wr, wc) owns W rows 64 wr .. and draft rows 16 CB wc .. (CB 16-row
+// column blocks of the MFMA B operand).
+template <int WC, int CB>
+struct GemmShape {
+  static constexpr int kWaves = 2 * WC;
+  static constexpr int kThreads = kWaves * kWave;
+  static constexpr int kDraftRows = WC * 16 * CB;
+  static constexpr int kRowsPerPass = kThreads / kGemmKC;     // staged rows per pass
+  static constexpr int kWPasses = kGemmRows / kRowsPerPass;   // W chunks per thread and step
+  static constexpr int kHPasses = kDraftRows / kRowsPerPass;  // h chunks per thread and step
+  static_assert(kWPasses * kRowsPerPass == kGemmRows && kHPasses * kRowsPerPass == kDraftRows,
+                "the staging passes must tile both operands");
+};
+
+template <int WC, int CB>
 struct GemmStage {
   u32x4 w[kGemmRows * kGemmPitch];
-  u32x4 h[kGemmRows * kGemmPitch];
+  u32x4 h[GemmShape<WC, CB>::kDraftRows * kGemmPitch];
 };
 
 // Slot of 16-byte chunk c of staged row r. The chunk index is XOR-swizzled
@@ -1227,21 +1242,40 @@ struct GemmStage {
 static_assert(kGemmKC == 8, "the swizzle permutes the 8 chunks of a row");
 __device__ __forceinline__ int gemm_slot(int r, int c) { return r * kGemmPitch + (c ^ (r & 7)); }
 
-// kShared: more than one pair of row groups, so each pair of W tiles is read
-// by several workgroups of one XCD (plain loads keep it in L2 for them).
-template <bool kShared>
-__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2)))
+// The quad-transposed draw for column blocks I .. CB - 1 of a wave's
+// accumulators (blocks past M skipped), expanded at compile time so that
+// every accumulator index is static.
+template <int I, int CB>
+__device__ __forceinline__ void draw_blocks(const HeadArgs &a, const f32x4 (&acc)[4][CB], int mw0,
+                                            int tile, int trow0, const int32_t (&fid)[4][4]) {
+  if constexpr (I < CB) {
+    if (mw0 + 16 * I < a.M) {  // uniform: the block has rows
+      const f32x4 z[4] = {acc[0][I], acc[1][I], acc[2][I], acc[3][I]};
+      quad_draw_publish(a, mw0 + 16 * I, tile, trow0, z, fid);
+    }
+    draw_blocks<I + 1, CB>(a, acc, mw0, tile, trow0, fid);
+  }
+}
+
+// kShared: more than one group of draft rows, so each pair of W tiles is
+// read by several workgroups of one XCD (plain loads keep it in L2 for
+// them); otherwise W is streamed once, non-temporally.
+template <bool kShared, int WC, int CB>
+__global__ __launch_bounds__((GemmShape<WC, CB>::kThreads)) __attribute__((amdgpu_waves_per_eu(2)))
 void head_gemm_kernel(HeadArgs a) {
-  __shared__ GemmStage sm[2];
+  using Shape = GemmShape<WC, CB>;
+  constexpr int kDR = Shape::kDraftRows, kRP = Shape::kRowsPerPass;
+  constexpr int kWP = Shape::kWPasses, kHP = Shape::kHPasses;
+  __shared__ GemmStage<WC, CB> sm[2];
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
-  const int tpairs = (a.tiles + 1) / 2, gpairs = (a.M + kGemmRows - 1) / kGemmRows;
+  const int tpairs = (a.tiles + 1) / 2, gpairs = (a.M + kDR - 1) / kDR;
   // Workgroup -> (tile pair p, row-group pair q): the pairs q of one p take
   // consecutive slots of one XCD, so that the W rows come from HBM once.
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
   const int q = slot % gpairs, p = xcd + 8 * (slot / gpairs);
   if (p >= tpairs) return;
   const int c16 = a.c16;
-  const int wrow0 = p * kGemmRows, mrow0 = q * kGemmRows;
+  const int wrow0 = p * kGemmRows, mrow0 = q * kDR;
   // Buffer resources over the rows that exist: W rows past V_high and draft
   // rows past M read as zero.
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
@@ -1249,87 +1283,113 @@ void head_gemm_kernel(HeadArgs a) {
       min(kGemmRows, a.V_high - wrow0) * c16 * 16, kBufferRsrcWord3);
   const __amdgpu_buffer_rsrc_t hres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<u32x4 *>(a.h + (size_t)mrow0 * c16), 0,
-      min(kGemmRows, a.M - mrow0) * c16 * 16, kBufferRsrcWord3);
-  // Thread tid stages chunk tid % 8 of rows tid / 8 + 32 j, j = 0..3, of
-  // both operands (8 lanes read one row's 128 bytes).
+      min(kDR, a.M - mrow0) * c16 * 16, kBufferRsrcWord3);
+  // Thread tid stages chunk tid % 8 of rows tid / 8 + kRP j of both
+  // operands (8 lanes read one row's 128 bytes).
   const int lr = tid >> 3, lc = tid & 7;
   const int steps = (c16 + kGemmKC - 1) / kGemmKC;
-  // Two steps in flight: register sets x (even steps) and y (odd steps).
-  // Every load is issued (a step past the last re-reads the last one), so
-  // the number of loads in flight is fixed and each wait covers one set.
-  u32x4 xw[4], xh[4], yw[4], yh[4];
-  auto load = [&](u32x4 (&vw)[4], u32x4 (&vh)[4], int s) {
-    // chunks past d are zeroed when staged
-    const int ch = min(min(s, steps - 1) * kGemmKC + lc, c16 - 1);
+  // W (from HBM) runs two steps ahead in register sets x (even steps) and y
+  // (odd steps). h (from L2) runs one step ahead in one set (kH2: also two,
+  // in sets hv and hv2, where the registers allow it: the 4-wave shape).
+  // Every load is issued (a step past the last re-reads the last one), and
+  // the loads a step waits for are always the oldest ones in flight: with
+  // one h set the h loads of step s + 1 go out before the W loads of s + 2.
+  constexpr bool kH2 = WC == 2;
+  u32x4 xw[kWP], yw[kWP], hv[kHP], hv2[kH2 ? kHP : 1];
+  auto chunk_of = [&](int s) {  // chunks past d are zeroed when staged
+    return min(min(s, steps - 1) * kGemmKC + lc, c16 - 1);
+  };
+  auto load_w = [&](u32x4 (&vw)[kWP], int s) {
+    const int ch = chunk_of(s);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int off = ((lr + 32 * j) * c16 + ch) * 16;
+    for (int j = 0; j < kWP; ++j) {
+      const int off = ((lr + kRP * j) * c16 + ch) * 16;
       vw[j] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, off, 0, kShared ? 0 : kCpolNt));
+    }
+  };
+  auto load_h = [&](u32x4 *vh, int s) {
+    const int ch = chunk_of(s);
+#pragma unroll
+    for (int j = 0; j < kHP; ++j) {
+      const int off = ((lr + kRP * j) * c16 + ch) * 16;
       vh[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hres, off, 0, 0));
     }
   };
-  const int wr = wave >> 1, wc = wave & 1;
+  const int wr = wave & 1, wc = wave >> 1;
   const int g = lane >> 4, r16 = lane & 15;
-  f32x4 acc[4][4];
+  f32x4 acc[4][CB];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // One step: its registers go to LDS buffer s % 2, then (after the
-  // barrier) the same registers are refilled with step s + 2 and the MFMAs
-  // run on the buffer.
-  auto do_step = [&](u32x4 (&vw)[4], u32x4 (&vh)[4], int s) {
-    GemmStage &st = sm[s & 1];
+  // barrier) h is refilled with step s + 1 and vw with step s + 2, and the
+  // MFMAs run on the buffer.
+  auto do_step = [&](u32x4 (&vw)[kWP], u32x4 *vh, int s) {
+    GemmStage<WC, CB> &st = sm[s & 1];
     const bool in = s * kGemmKC + lc < c16;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      st.w[gemm_slot(lr + 32 * j, lc)] = in ? vw[j] : u32x4{0, 0, 0, 0};
-      st.h[gemm_slot(lr + 32 * j, lc)] = in ? vh[j] : u32x4{0, 0, 0, 0};
-    }
+    for (int j = 0; j < kWP; ++j) st.w[gemm_slot(lr + kRP * j, lc)] = in ? vw[j] : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < kHP; ++j) st.h[gemm_slot(lr + kRP * j, lc)] = in ? vh[j] : u32x4{0, 0, 0, 0};
     // The stage is complete, and every wave is done with the buffer the
     // next stage overwrites (it read it two stages ago).
     __syncthreads();
-    // The scheduling barriers keep every set's loads in issue order (set x
-    // before set y), which lets each wait cover one set only.
+    // The scheduling barriers keep the loads in issue order, which lets
+    // each wait cover the oldest loads only.
     __builtin_amdgcn_sched_barrier(0);
-    load(vw, vh, s + 2);
+    if constexpr (kH2) {
+      load_w(vw, s + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      load_h(vh, s + 2);
+    } else {
+      load_h(vh, s + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(vw, s + 2);
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < kGemmKC / 4; ++t) {
       const int cl = 4 * t + g;
-      u32x4 av[4], bv[4];
+      u32x4 av[4];
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) av[rb] = st.w[gemm_slot(64 * wr + 16 * rb + r16, cl)];
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) bv[cb] = st.h[gemm_slot(64 * wc + 16 * cb + r16, cl)];
+      for (int cb = 0; cb < CB; ++cb) {
+        const u32x4 bv = st.h[gemm_slot(16 * CB * wc + 16 * cb + r16, cl)];
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
+        for (int rb = 0; rb < 4; ++rb)
           acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, av[rb]), __builtin_bit_cast(bf16x8, bv[cb]),
-              acc[rb][cb], 0, 0, 0);
+              __builtin_bit_cast(bf16x8, av[rb]), __builtin_bit_cast(bf16x8, bv), acc[rb][cb],
+              0, 0, 0);
+      }
     }
   };
-  load(xw, xh, 0);
+  load_w(xw, 0);
   __builtin_amdgcn_sched_barrier(0);
-  load(yw, yh, 1);
+  load_h(hv, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(yw, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (kH2) load_h(hv2, 1);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll 1
   for (int s = 0; s < steps; s += 2) {
-    do_step(xw, xh, s);
-    do_step(yw, yh, s + 1);  // past the last step: every chunk is zeroed
+    do_step(xw, hv, s);
+    do_step(yw, kH2 ? hv2 : hv, s + 1);  // past the last step: every chunk is zeroed
   }
 
   // Epilogue of wave (wr, wc): lane (g, r16) holds, per (rb, cb), the
   // logits of tile rows 16 rb + 4 g .. + 3 for draft row 16 cb + r16.
   const int tile = 2 * p + wr;
   const int trow0 = tile * kTileRows;
-  const int mw0 = mrow0 + 64 * wc;  // the wave's first draft row
-  if (a.sample) {
-    // Sampling: the quad-transposed draw per 16-row column block.
+  const int mw0 = mrow0 + 16 * CB * wc;  // the wave's first draft row
+  // Sampling: the quad-transposed draw per 16-row column block (not
+  // compiled for 8 blocks per wave, whose registers it would overflow; the
+  // host runs draws on narrower shapes).
+  if constexpr (CB <= 4) if (a.sample) {
     if (tile >= a.tiles) return;
     int32_t fid[4][4];
 #pragma unroll
@@ -1340,25 +1400,20 @@ void head_gemm_kernel(HeadArgs a) {
         fid[rb][i] = row < a.V_high ? fid_at(a, row) : 0;
         if (a.bias && row < a.V_high)
 #pragma unroll
-          for (int cb = 0; cb < 4; ++cb) acc[rb][cb][i] += bf16_to_f32(a.bias[row]);
+          for (int cb = 0; cb < CB; ++cb) acc[rb][cb][i] += bf16_to_f32(a.bias[row]);
       }
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      if (mw0 + 16 * cb >= a.M) break;  // uniform: no row of this block exists
-      const f32x4 z[4] = {acc[0][cb], acc[1][cb], acc[2][cb], acc[3][cb]};
-      quad_draw_publish(a, mw0 + 16 * cb, tile, trow0, z, fid);
-    }
+    draw_blocks<0, CB>(a, acc, mw0, tile, trow0, fid);
     return;
   }
   if (tile >= a.tiles) return;
   // Over the wave's draft rows that exist, from this tile on (none: no
   // stores follow).
-  const int zrows = min(64, a.M - mw0);
+  const int zrows = min(16 * CB, a.M - mw0);
   const __amdgpu_buffer_rsrc_t zres = __builtin_amdgcn_make_buffer_rsrc(
       a.zbuf + (size_t)max(0, min(mw0, a.M - 1)) * a.zpitch + trow0, 0,
       zrows > 0 ? (int)(((size_t)zrows * a.zpitch - trow0) * 4) : 0, kBufferRsrcWord3);
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
+  for (int cb = 0; cb < CB; ++cb) {
     const int m = mw0 + 16 * cb + r16;
     float mx = -INFINITY;
 #pragma unroll
@@ -1395,14 +1450,34 @@ void head_gemm_kernel(HeadArgs a) {
   }
 }
 
-hipError_t launch_gemm(const HeadArgs &a, hipStream_t stream) {
-  const int tpairs = (a.tiles + 1) / 2, gpairs = (a.M + kGemmRows - 1) / kGemmRows;
-  const dim3 grid(8 * ((tpairs + 7) / 8) * gpairs), block(kGemmThreads);
+template <int WC, int CB>
+hipError_t launch_gemm_shape(const HeadArgs &a, hipStream_t stream) {
+  using Shape = GemmShape<WC, CB>;
+  const int tpairs = (a.tiles + 1) / 2, gpairs = (a.M + Shape::kDraftRows - 1) / Shape::kDraftRows;
+  const dim3 grid(8 * ((tpairs + 7) / 8) * gpairs), block(Shape::kThreads);
   if (gpairs > 1)
-    hipLaunchKernelGGL((head_gemm_kernel<true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((head_gemm_kernel<true, WC, CB>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((head_gemm_kernel<false>), grid, block, 0, stream, a);
-  hipError_t e = hipGetLastError();
+    hipLaunchKernelGGL((head_gemm_kernel<false, WC, CB>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+// Past 64 draft rows: one workgroup per pair of W tiles covers every draft
+// row (up to 512), so that W_trim is streamed from memory exactly once; the
+// workgroup grows with M (4 waves of 64 x 64 up to 128 rows, 8 waves of
+// 64 x 64 up to 256, of 64 x 96 up to 384 and of 64 x 128 up to 512).
+// Draws past 256 rows run groups of 256 rows on the 64 x 64 shape (the draw
+// does not fit the registers next to 6 or 8 column blocks).
+hipError_t launch_gemm(const HeadArgs &a, hipStream_t stream) {
+  hipError_t e;
+  if (a.M <= 128)
+    e = launch_gemm_shape<2, 4>(a, stream);
+  else if (a.M <= 256 || a.sample)
+    e = launch_gemm_shape<4, 4>(a, stream);
+  else if (a.M <= 384)
+    e = launch_gemm_shape<4, 6>(a, stream);
+  else
+    e = launch_gemm_shape<4, 8>(a, stream);
   if (e != hipSuccess) return e;
   if (a.sample)
     hipLaunchKernelGGL((head_merge_kernel<8>), dim3(a.M), dim3(8 * kWave), 0, stream, a);
