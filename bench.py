@@ -96,6 +96,17 @@ def median_us(fn, reps, torch):
     return statistics.median(ts)
 
 
+def head_kernels(M, V_high):
+    """The kernels one draft-head call launches (the library's dispatch)."""
+    if M <= 2:
+        return "head_gemv_kernel"
+    tile_pairs = (V_high + 127) // 128
+    if M > 64 or tile_pairs >= 256:
+        return "head_gemm_kernel + tree_merge_kernel"
+    return ("head_mfma_kernel + tree_merge_kernel" if M <= 32 else
+            "h_pack_kernel + head_mfma_kernel + tree_merge_kernel")
+
+
 def recorded_traffic():
     """HBM bytes per launch of the head kernel from the committed counter
     summary, or None if the kernel sources changed since it was taken."""
@@ -393,9 +404,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic() if (w.name == "llama3_8b" and M == 1) else None,
-                     "kernel": "head_gemv_kernel" if M <= 2 else
-                               ("head_mfma_kernel + tree_merge_kernel" if M <= 32 else
-                                "h_pack_kernel + head_mfma_kernel + tree_merge_kernel"),
+                     "kernel": head_kernels(M, V_high),
                      "bytes_per_launch": nb,
                      "us_per_launch": round(ms_step * 1000, 3),
                      "us_single_launch_events": round(us_launch, 3)},

@@ -11,13 +11,15 @@
 //     workgroup that finishes last (atomic ticket) reads every partial once
 //     and merges them: the softmax partials in a fixed order, the keys by a
 //     threshold filter and a rank, so results do not depend on scheduling.
-//   * 3 <= M <= 64: a skinny GEMM on the matrix cores (head_mfma_kernel; past
-//     32 rows h_pack_kernel first lays h out in operand order), which writes
-//     each tile's fp32 logits and softmax partials to the workspace, then one
-//     merge workgroup per draft row (tree_merge_kernel) that reads the
-//     partials and the logits of only the tiles that can hold a pick.
-//   * M > 64: a GEMM tiling of 128 x 128 blocks (head_gemm_kernel), then the
-//     same per-row merge.
+//   * 3 <= M <= 512: a GEMM tiling on the matrix cores (head_gemm_kernel: one
+//     8-wave workgroup per pair of W tiles over every draft row, both
+//     operands copied into an LDS ring), which writes each tile's fp32
+//     logits and softmax partials to the workspace, then one merge workgroup
+//     per draft row (tree_merge_kernel) that reads the partials and the
+//     logits of only the tiles that can hold a pick. Up to 64 rows on a
+//     head of fewer than 512 tiles (too few tile pairs to fill the chip) a
+//     skinny GEMM with one workgroup per tile (head_mfma_kernel; past 32
+//     rows h_pack_kernel first lays h out in operand order) takes its place.
 // Sampling (one draw per row) runs the same contraction kernels with a
 // per-tile draw in place of the logits. Up to M of about 312 the head is
 // bound by HBM bandwidth: it moves 2 * V_high * d bytes of W_trim for
@@ -962,6 +964,7 @@ __global__ __launch_bounds__(kWave) void h_pack_kernel(const u32x4 *__restrict__
 template <int NT>
 constexpr bool kDirectH = NT <= 2;
 
+
 // Up to 64 draft rows, one workgroup per tile; each W tile is read once and
 // streams past the caches (non-temporal loads; plain ones cost 4.5 us at
 // M = 60).
@@ -1198,49 +1201,24 @@ __global__ __launch_bounds__(WAVES *kWave) void tree_merge_kernel(HeadArgs a) {
 }
 
 // ------------------------------------------- MFMA path, many draft rows
-// Past 64 draft rows the contraction is tiled as a GEMM: a
-// workgroup of 4 waves computes 128 W rows (two tiles) x 128 draft rows (two
-// groups of 64). Per K step of 64 both operand tiles (128 rows x 128 bytes
-// each, W from W_trim, the B operand straight from h) are staged in LDS,
-// double buffered with one barrier per step, and wave (wr, wc) owns the
-// 64 x 64 block of tile 2 p + wr and row group 2 q + wc over the whole of d,
-// so it ends with final sums: logits and the (draft row, tile) softmax
-// partials (or the tile's draws) go out as on the 64-row path and the same
-// row merges follow.
-// Against one 64 x 64 block per workgroup this halves the L2 traffic per
-// flop, which bounds the contraction at these sizes.
-constexpr int kGemmRows = 128;               // W rows per workgroup
-constexpr int kGemmKC = 8;                   // 16-byte chunks per row and K step
-constexpr int kGemmPitch = kGemmKC;          // staged row pitch in chunks (swizzled)
+// The contraction tiled as a GEMM: one workgroup of 8 waves per pair of W
+// tiles (128 W rows) covers up to 64 CB draft rows, so that W_trim streams
+// from memory once. Wave (wr, wc) owns the 64 x 16 CB block of tile 2 p + wr
+// and draft rows 16 CB wc .. over the whole of d, so it ends with final
+// sums: logits and the (draft row, tile) softmax partials (or the tile's
+// draws) go out as on the 64-row path and the same row merges follow.
+constexpr int kGemmRows = 128;                  // W rows per workgroup
+constexpr int kGemmKC = 8;                      // 16-byte chunks per row and K step
+constexpr int kGemmWaves = 8;
+constexpr int kGemmThreads = kGemmWaves * kWave;
 
-// A workgroup of 2 x WC waves covers 128 W rows and WC x 16 CB draft rows:
-// wave (wr, wc) owns W rows 64 wr .. and draft rows 16 CB wc .. (CB 16-row
-// column blocks of the MFMA B operand).
-template <int WC, int CB>
-struct GemmShape {
-  static constexpr int kWaves = 2 * WC;
-  static constexpr int kThreads = kWaves * kWave;
-  static constexpr int kDraftRows = WC * 16 * CB;
-  static constexpr int kRowsPerPass = kThreads / kGemmKC;     // staged rows per pass
-  static constexpr int kWPasses = kGemmRows / kRowsPerPass;   // W chunks per thread and step
-  static constexpr int kHPasses = kDraftRows / kRowsPerPass;  // h chunks per thread and step
-  static_assert(kWPasses * kRowsPerPass == kGemmRows && kHPasses * kRowsPerPass == kDraftRows,
-                "the staging passes must tile both operands");
-};
-
-template <int WC, int CB>
-struct GemmStage {
-  u32x4 w[kGemmRows * kGemmPitch];
-  u32x4 h[GemmShape<WC, CB>::kDraftRows * kGemmPitch];
-};
-
-// Slot of 16-byte chunk c of staged row r. The chunk index is XOR-swizzled
-// by the row's low three bits: the operand reads (16 rows at one chunk for
-// each of four chunks per instruction) then hit distinct banks. Measured
-// with the LDS counters: 4 cycles per read instruction against 8 for an
-// unswizzled row pitch of 9 chunks.
+// Slot of 16-byte chunk c of staged row r (rows of 8 chunks). The chunk index
+// is XOR-swizzled by the row's low three bits: the operand reads (16 rows at
+// one chunk for each of four chunks per instruction) then hit distinct banks.
+// Measured with the LDS counters: 4 cycles per read instruction against 8 for
+// an unswizzled row pitch of 9 chunks.
 static_assert(kGemmKC == 8, "the swizzle permutes the 8 chunks of a row");
-__device__ __forceinline__ int gemm_slot(int r, int c) { return r * kGemmPitch + (c ^ (r & 7)); }
+__device__ __forceinline__ int gemm_slot(int r, int c) { return r * kGemmKC + (c ^ (r & 7)); }
 
 // The quad-transposed draw for column blocks I .. CB - 1 of a wave's
 // accumulators (blocks past M skipped), expanded at compile time so that
@@ -1257,135 +1235,14 @@ __device__ __forceinline__ void draw_blocks(const HeadArgs &a, const f32x4 (&acc
   }
 }
 
-// kShared: more than one group of draft rows, so each pair of W tiles is
-// read by several workgroups of one XCD (plain loads keep it in L2 for
-// them); otherwise W is streamed once, non-temporally.
-template <bool kShared, int WC, int CB>
-__global__ __launch_bounds__((GemmShape<WC, CB>::kThreads)) __attribute__((amdgpu_waves_per_eu(2)))
-void head_gemm_kernel(HeadArgs a) {
-  using Shape = GemmShape<WC, CB>;
-  constexpr int kDR = Shape::kDraftRows, kRP = Shape::kRowsPerPass;
-  constexpr int kWP = Shape::kWPasses, kHP = Shape::kHPasses;
-  __shared__ GemmStage<WC, CB> sm[2];
-  const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
-  const int tpairs = (a.tiles + 1) / 2, gpairs = (a.M + kDR - 1) / kDR;
-  // Workgroup -> (tile pair p, row-group pair q): the pairs q of one p take
-  // consecutive slots of one XCD, so that the W rows come from HBM once.
-  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
-  const int q = slot % gpairs, p = xcd + 8 * (slot / gpairs);
-  if (p >= tpairs) return;
-  const int c16 = a.c16;
-  const int wrow0 = p * kGemmRows, mrow0 = q * kDR;
-  // Buffer resources over the rows that exist: W rows past V_high and draft
-  // rows past M read as zero.
-  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<u32x4 *>(a.W + (size_t)wrow0 * c16), 0,
-      min(kGemmRows, a.V_high - wrow0) * c16 * 16, kBufferRsrcWord3);
-  const __amdgpu_buffer_rsrc_t hres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<u32x4 *>(a.h + (size_t)mrow0 * c16), 0,
-      min(kDR, a.M - mrow0) * c16 * 16, kBufferRsrcWord3);
-  // Thread tid stages chunk tid % 8 of rows tid / 8 + kRP j of both
-  // operands (8 lanes read one row's 128 bytes).
-  const int lr = tid >> 3, lc = tid & 7;
-  const int steps = (c16 + kGemmKC - 1) / kGemmKC;
-  // W (from HBM) runs two steps ahead in register sets x (even steps) and y
-  // (odd steps). h (from L2) runs one step ahead in one set (kH2: also two,
-  // in sets hv and hv2, where the registers allow it: the 4-wave shape).
-  // Every load is issued (a step past the last re-reads the last one), and
-  // the loads a step waits for are always the oldest ones in flight: with
-  // one h set the h loads of step s + 1 go out before the W loads of s + 2.
-  constexpr bool kH2 = WC == 2;
-  u32x4 xw[kWP], yw[kWP], hv[kHP], hv2[kH2 ? kHP : 1];
-  auto chunk_of = [&](int s) {  // chunks past d are zeroed when staged
-    return min(min(s, steps - 1) * kGemmKC + lc, c16 - 1);
-  };
-  auto load_w = [&](u32x4 (&vw)[kWP], int s) {
-    const int ch = chunk_of(s);
-#pragma unroll
-    for (int j = 0; j < kWP; ++j) {
-      const int off = ((lr + kRP * j) * c16 + ch) * 16;
-      vw[j] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, off, 0, kShared ? 0 : kCpolNt));
-    }
-  };
-  auto load_h = [&](u32x4 *vh, int s) {
-    const int ch = chunk_of(s);
-#pragma unroll
-    for (int j = 0; j < kHP; ++j) {
-      const int off = ((lr + kRP * j) * c16 + ch) * 16;
-      vh[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hres, off, 0, 0));
-    }
-  };
-  const int wr = wave & 1, wc = wave >> 1;
-  const int g = lane >> 4, r16 = lane & 15;
-  f32x4 acc[4][CB];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // One step: its registers go to LDS buffer s % 2, then (after the
-  // barrier) h is refilled with step s + 1 and vw with step s + 2, and the
-  // MFMAs run on the buffer.
-  auto do_step = [&](u32x4 (&vw)[kWP], u32x4 *vh, int s) {
-    GemmStage<WC, CB> &st = sm[s & 1];
-    const bool in = s * kGemmKC + lc < c16;
-#pragma unroll
-    for (int j = 0; j < kWP; ++j) st.w[gemm_slot(lr + kRP * j, lc)] = in ? vw[j] : u32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int j = 0; j < kHP; ++j) st.h[gemm_slot(lr + kRP * j, lc)] = in ? vh[j] : u32x4{0, 0, 0, 0};
-    // The stage is complete, and every wave is done with the buffer the
-    // next stage overwrites (it read it two stages ago).
-    __syncthreads();
-    // The scheduling barriers keep the loads in issue order, which lets
-    // each wait cover the oldest loads only.
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (kH2) {
-      load_w(vw, s + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      load_h(vh, s + 2);
-    } else {
-      load_h(vh, s + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      load_w(vw, s + 2);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int t = 0; t < kGemmKC / 4; ++t) {
-      const int cl = 4 * t + g;
-      u32x4 av[4];
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) av[rb] = st.w[gemm_slot(64 * wr + 16 * rb + r16, cl)];
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const u32x4 bv = st.h[gemm_slot(16 * CB * wc + 16 * cb + r16, cl)];
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, av[rb]), __builtin_bit_cast(bf16x8, bv), acc[rb][cb],
-              0, 0, 0);
-      }
-    }
-  };
-  load_w(xw, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  load_h(hv, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  load_w(yw, 1);
-  __builtin_amdgcn_sched_barrier(0);
-  if constexpr (kH2) load_h(hv2, 1);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll 1
-  for (int s = 0; s < steps; s += 2) {
-    do_step(xw, hv, s);
-    do_step(yw, kH2 ? hv2 : hv, s + 1);  // past the last step: every chunk is zeroed
-  }
-
-  // Epilogue of wave (wr, wc): lane (g, r16) holds, per (rb, cb), the
-  // logits of tile rows 16 rb + 4 g .. + 3 for draft row 16 cb + r16.
+// Epilogue of wave (wr, wc) of a GEMM-tiled workgroup over W tile pair p,
+// whose first draft row is mw0: lane (g, r16) holds, per (rb, cb), the
+// logits of tile rows 16 rb + 4 g .. + 3 for draft row mw0 + 16 cb + r16.
+template <int CB>
+__device__ __forceinline__ void gemm_epilogue(const HeadArgs &a, f32x4 (&acc)[4][CB], int p,
+                                              int wr, int mw0, int g, int r16) {
   const int tile = 2 * p + wr;
   const int trow0 = tile * kTileRows;
-  const int mw0 = mrow0 + 16 * CB * wc;  // the wave's first draft row
   // Sampling: the quad-transposed draw per 16-row column block (not
   // compiled for 8 blocks per wave, whose registers it would overflow; the
   // host runs draws on narrower shapes).
@@ -1450,34 +1307,178 @@ void head_gemm_kernel(HeadArgs a) {
   }
 }
 
-template <int WC, int CB>
+// Up to 64 draft rows the GEMM tiling takes over from the 64-row kernel once
+// its workgroups (one per pair of W tiles) fill the chip's 256 CUs; with
+// fewer the 64-row kernel's one workgroup per tile keeps more CUs streaming.
+constexpr int kRingMinPairs = 256;
+
+// Both operands are copied from memory straight into LDS (buffer loads with
+// the LDS flag: each lane's 16 bytes land in slot lane of a 64-slot block, no
+// registers involved), through a ring of S stages, so that S - 1 K steps are
+// in flight per workgroup at no register cost. A stage holds the 128 W rows,
+// then the draft rows, 8 chunks each in the swizzled order of gemm_slot; lane
+// l of a load fills row l / 8 of its 8-row block at position l % 8, so it
+// reads chunk (l % 8) ^ (l / 8) of that row. Chunks past d and rows past
+// V_high or M are addressed outside the buffer ranges, which the hardware
+// turns into zeros in LDS.
+template <int CB, int S>
+struct GemmRing {
+  static constexpr int kDraftRows = 4 * 16 * CB;
+  static constexpr int kSlots = (kGemmRows + kDraftRows) * kGemmKC;  // per stage
+  static constexpr int kLoads = (kGemmRows + kDraftRows) / 8 / kGemmWaves;
+  static constexpr int kWLoads = kGemmRows / 8 / kGemmWaves;
+  static_assert(kLoads * 8 * kGemmWaves == kGemmRows + kDraftRows &&
+                    kWLoads * 8 * kGemmWaves == kGemmRows,
+                "every wave issues whole 8-row blocks of each operand");
+  static_assert(S >= 2 && (S - 1) * kLoads <= 63, "the in-flight loads must fit vmcnt");
+  static_assert(S * kSlots * 16 <= 160 * 1024, "the ring must fit the LDS");
+};
+
+// s_waitcnt on the vector-memory counter alone (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, the other counters at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// kShared: more than one group of draft rows, so each pair of W tiles is
+// read by two workgroups of one XCD (plain loads keep it in L2 for the
+// other); otherwise W is streamed once, non-temporally.
+template <bool kShared, int CB, int S>
+__global__ __launch_bounds__(kGemmThreads) void head_gemm_kernel(HeadArgs a) {
+  using Ring = GemmRing<CB, S>;
+  constexpr int kDR = Ring::kDraftRows, kWaves = kGemmWaves;
+  constexpr int kLoads = Ring::kLoads, kWLoads = Ring::kWLoads, kSlots = Ring::kSlots;
+  __shared__ u32x4 ring[S * kSlots];
+  // The wave index is uniform (the LDS address of a load must be).
+  const int tid = threadIdx.x, lane = __lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int tpairs = (a.tiles + 1) / 2, gpairs = (a.M + kDR - 1) / kDR;
+  // Workgroup -> (tile pair p, draft-row group q); past 256 draft rows (draws
+  // only) the groups of one tile pair take consecutive slots of one XCD, so
+  // that the later one finds the W rows in that XCD's L2.
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int q = slot % gpairs, p = xcd + 8 * (slot / gpairs);
+  if (p >= tpairs) return;
+  const int c16 = a.c16;
+  const int wrow0 = p * kGemmRows, mrow0 = q * kDR;
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u32x4 *>(a.W + (size_t)wrow0 * c16), 0,
+      min(kGemmRows, a.V_high - wrow0) * c16 * 16, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t hres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u32x4 *>(a.h + (size_t)mrow0 * c16), 0,
+      min(kDR, a.M - mrow0) * c16 * 16, kBufferRsrcWord3);
+  const int lrow = lane >> 3, lchunk = (lane & 7) ^ lrow;
+  // Load j of this wave fills 8-row block wave + kWaves j of a stage: W
+  // rows for j < kWLoads, draft rows after them.
+  uint32_t voff[kLoads];
+#pragma unroll
+  for (int j = 0; j < kLoads; ++j) {
+    const int blk = wave + kWaves * j;
+    const int row = 8 * (j < kWLoads ? blk : blk - kGemmRows / 8) + lrow;
+    voff[j] = (uint32_t)(row * c16 + lchunk) * 16u;
+  }
+  // Workgroups start their K loop at staggered steps (tile pair p at step
+  // p mod steps) and wrap around, so that at any moment the rows in flight
+  // are spread over the whole width of d. In step with one another they
+  // would all read the same 128-byte column of 8 KiB-strided rows and crowd
+  // onto a few memory channels: measured, the stagger takes M = 60 from 67
+  // to 49 us and M = 128 from 67 to 56 us.
+  const int steps = (c16 + kGemmKC - 1) / kGemmKC;
+  const int rot = p % steps;
+  // K step s (the workgroup's s-th, step se of d) into ring stage s % S;
+  // every step is issued, steps past the last (and chunks past d) as
+  // out-of-range zero loads.
+  auto issue = [&](int s) {
+    const int se = s < steps ? (s + rot < steps ? s + rot : s + rot - steps) : s;
+    // All ones past d, else zero (arithmetic, so that no lane branches).
+    const uint32_t past = ~(uint32_t)((se * kGemmKC + lchunk - c16) >> 31);
+    u32x4 *stage = ring + (s % S) * kSlots;
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const uint32_t off = (voff[j] + (uint32_t)se * (kGemmKC * 16)) | (past & 0x7fffff00u);
+      auto *dst = (__attribute__((address_space(3))) void *)(stage + 64 * (wave + kWaves * j));
+      if (j < kWLoads)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, dst, 16, off, 0, 0, kShared ? 0 : kCpolNt);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(hres, dst, 16, off, 0, 0, 0);
+    }
+  };
+  const int wr = wave & 1, wc = wave >> 1;
+  const int g = lane >> 4, r16 = lane & 15;
+  f32x4 acc[4][CB];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s) issue(s);
+#pragma unroll 1
+  for (int s = 0; s < steps; ++s) {
+    // This wave's loads of step s have landed (the S - 2 later steps may
+    // still be in flight) and its reads of the previous stage have
+    // returned; after the barrier every wave's loads of step s have, and no
+    // wave reads the stage that the next issue overwrites.
+    wait_vmcnt<(S - 2) * kLoads>();
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(s + S - 1);
+    const u32x4 *st = ring + (s % S) * kSlots;
+#pragma unroll
+    for (int t = 0; t < kGemmKC / 4; ++t) {
+      const int cl = 4 * t + g;
+      u32x4 av[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) av[rb] = st[gemm_slot(64 * wr + 16 * rb + r16, cl)];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const u32x4 bv = st[kGemmRows * kGemmKC + gemm_slot(16 * CB * wc + 16 * cb + r16, cl)];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, av[rb]), __builtin_bit_cast(bf16x8, bv), acc[rb][cb],
+              0, 0, 0);
+      }
+    }
+  }
+  // No load into this workgroup's LDS may outlive it.
+  wait_vmcnt<0>();
+  gemm_epilogue<CB>(a, acc, p, wr, mrow0 + 16 * CB * wc, g, r16);
+}
+
+template <int CB, int S>
 hipError_t launch_gemm_shape(const HeadArgs &a, hipStream_t stream) {
-  using Shape = GemmShape<WC, CB>;
-  const int tpairs = (a.tiles + 1) / 2, gpairs = (a.M + Shape::kDraftRows - 1) / Shape::kDraftRows;
-  const dim3 grid(8 * ((tpairs + 7) / 8) * gpairs), block(Shape::kThreads);
+  const int tpairs = (a.tiles + 1) / 2;
+  const int gpairs = (a.M + GemmRing<CB, S>::kDraftRows - 1) / GemmRing<CB, S>::kDraftRows;
+  const dim3 grid(8 * ((tpairs + 7) / 8) * gpairs), block(kGemmThreads);
   if (gpairs > 1)
-    hipLaunchKernelGGL((head_gemm_kernel<true, WC, CB>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((head_gemm_kernel<true, CB, S>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((head_gemm_kernel<false, WC, CB>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((head_gemm_kernel<false, CB, S>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
-// Past 64 draft rows: one workgroup per pair of W tiles covers every draft
-// row (up to 512), so that W_trim is streamed from memory exactly once; the
-// workgroup grows with M (4 waves of 64 x 64 up to 128 rows, 8 waves of
-// 64 x 64 up to 256, of 64 x 96 up to 384 and of 64 x 128 up to 512).
-// Draws past 256 rows run groups of 256 rows on the 64 x 64 shape (the draw
-// does not fit the registers next to 6 or 8 column blocks).
+// The block of each wave grows with M: 64 x 16 up to 64 draft rows, 64 x 32
+// up to 128, 64 x 64 up to 256, 64 x 96 up to 384 and 64 x 128 up to 512,
+// with as many ring stages as fit the LDS (4, 4, 3, 2, 2). Draws past 256
+// rows run two groups of 256 rows on the 64 x 64 shape (the draw does not
+// fit the registers next to 6 or 8 column blocks).
 hipError_t launch_gemm(const HeadArgs &a, hipStream_t stream) {
   hipError_t e;
-  if (a.M <= 128)
+  if (a.M <= 64)
+    e = launch_gemm_shape<1, 4>(a, stream);
+  else if (a.M <= 128)
     e = launch_gemm_shape<2, 4>(a, stream);
   else if (a.M <= 256 || a.sample)
-    e = launch_gemm_shape<4, 4>(a, stream);
+    e = launch_gemm_shape<4, 3>(a, stream);
   else if (a.M <= 384)
-    e = launch_gemm_shape<4, 6>(a, stream);
+    e = launch_gemm_shape<6, 2>(a, stream);
   else
-    e = launch_gemm_shape<4, 8>(a, stream);
+    e = launch_gemm_shape<8, 2>(a, stream);
   if (e != hipSuccess) return e;
   if (a.sample)
     hipLaunchKernelGGL((head_merge_kernel<8>), dim3(a.M), dim3(8 * kWave), 0, stream, a);
@@ -1640,7 +1641,7 @@ hipError_t launch_head_call(const uint16_t *h, int32_t M, int32_t d, const uint1
   // more: the GEMM tiling of 128 x 128 blocks. Then one merge workgroup per
   // draft row.
   if (M <= kGemvMaxRows) return launch_gemv(a, stream);
-  if (M > kGroupRows) return launch_gemm(a, stream);
+  if (M > kGroupRows || (p.tiles + 1) / 2 >= kRingMinPairs) return launch_gemm(a, stream);
   switch ((M + 15) / 16) {
     case 1: return launch_mfma<1>(a, stream);
     case 2: return launch_mfma<2>(a, stream);
