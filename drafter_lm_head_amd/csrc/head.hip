@@ -1246,7 +1246,7 @@ __device__ __forceinline__ void gemm_epilogue(const HeadArgs &a, f32x4 (&acc)[4]
   // Sampling: the quad-transposed draw per 16-row column block (not
   // compiled for 8 blocks per wave, whose registers it would overflow; the
   // host runs draws on narrower shapes).
-  if constexpr (CB <= 4) if (a.sample) {
+  if constexpr (CB <= 6) if (a.sample) {
     if (tile >= a.tiles) return;
     int32_t fid[4][4];
 #pragma unroll
@@ -1355,7 +1355,7 @@ __global__ __launch_bounds__(kGemmThreads) void head_gemm_kernel(HeadArgs a) {
   const int tid = threadIdx.x, lane = __lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int tpairs = (a.tiles + 1) / 2, gpairs = (a.M + kDR - 1) / kDR;
-  // Workgroup -> (tile pair p, draft-row group q); past 256 draft rows (draws
+  // Workgroup -> (tile pair p, draft-row group q); past 384 draft rows (draws
   // only) the groups of one tile pair take consecutive slots of one XCD, so
   // that the later one finds the W rows in that XCD's L2.
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
@@ -1379,14 +1379,19 @@ __global__ __launch_bounds__(kGemmThreads) void head_gemm_kernel(HeadArgs a) {
     const int row = 8 * (j < kWLoads ? blk : blk - kGemmRows / 8) + lrow;
     voff[j] = (uint32_t)(row * c16 + lchunk) * 16u;
   }
-  // Workgroups start their K loop at staggered steps (tile pair p at step
-  // p mod steps) and wrap around, so that at any moment the rows in flight
-  // are spread over the whole width of d. In step with one another they
-  // would all read the same 128-byte column of 8 KiB-strided rows and crowd
-  // onto a few memory channels: measured, the stagger takes M = 60 from 67
-  // to 49 us and M = 128 from 67 to 56 us.
+  // Workgroups start their K loop at staggered steps and wrap around, so
+  // that at any moment the rows in flight are spread over the width of d. In
+  // step with one another they would all read the same 128-byte column of
+  // 8 KiB-strided rows and crowd onto a few memory channels. The workgroups
+  // of one XCD (tile pairs p, p + 8, ...) start one step apart, so that
+  // their columns cover all of that XCD's L2 channels; every XCD uses the
+  // same offsets, and the two row groups of a tile pair (draws past 384
+  // rows) the same one. Measured on the 4096 x 32768 head against no stagger: M = 60
+  // 67.4 -> 46.2 us, M = 128 68.7 -> 56.0 us; starting tile pair p at step
+  // p mod steps instead (8 distinct offsets per XCD) gave 49.6 and 56.6 us,
+  // and shifting alternate XCDs by half of d 72.6 and 77.7 us.
   const int steps = (c16 + kGemmKC - 1) / kGemmKC;
-  const int rot = p % steps;
+  const int rot = (p / 8) % steps;
   // K step s (the workgroup's s-th, step se of d) into ring stage s % S;
   // every step is issued, steps past the last (and chunks past d) as
   // out-of-range zero loads.
@@ -1464,16 +1469,16 @@ hipError_t launch_gemm_shape(const HeadArgs &a, hipStream_t stream) {
 
 // The block of each wave grows with M: 64 x 16 up to 64 draft rows, 64 x 32
 // up to 128, 64 x 64 up to 256, 64 x 96 up to 384 and 64 x 128 up to 512,
-// with as many ring stages as fit the LDS (4, 4, 3, 2, 2). Draws past 256
+// with as many ring stages as fit the LDS (4, 4, 3, 2, 2). Draws past 384
 // rows run two groups of 256 rows on the 64 x 64 shape (the draw does not
-// fit the registers next to 6 or 8 column blocks).
+// fit the registers next to 8 column blocks).
 hipError_t launch_gemm(const HeadArgs &a, hipStream_t stream) {
   hipError_t e;
   if (a.M <= 64)
     e = launch_gemm_shape<1, 4>(a, stream);
   else if (a.M <= 128)
     e = launch_gemm_shape<2, 4>(a, stream);
-  else if (a.M <= 256 || a.sample)
+  else if (a.M <= 256 || (a.sample && a.M > 384))
     e = launch_gemm_shape<4, 3>(a, stream);
   else if (a.M <= 384)
     e = launch_gemm_shape<6, 2>(a, stream);

@@ -63,8 +63,9 @@ def test_draft_rows(dlh, M):
 
 @pytest.mark.parametrize("M", [17, 33, 60, 64, 65, 100, 128, 257, 512])
 def test_draft_tree_rows(dlh, M):
-    # M > 2 runs the MFMA skinny GEMM and one merge workgroup per row; past
-    # 64 rows the workgroups take groups of 64 draft rows of each tile.
+    # On this small head (too few tile pairs for the GEMM tiling) up to 64
+    # rows run the 64-row MFMA kernel, past 64 the GEMM tiling; then one
+    # merge workgroup per row.
     h, W, t2f = rand_case(200 + M, M, 1024, 2500)
     check_case(dlh, h, W, t2f, 10)
 
@@ -82,6 +83,17 @@ def test_draft_tree_edges(dlh, V_high, d, k, M):
     # (d = 8) with packed h.
     h, W, t2f = rand_case(300 + V_high, M, d, V_high, hscale=2.0)
     check_case(dlh, h, W, t2f, min(k, V_high))
+
+
+@pytest.mark.parametrize("V_high,d,M", [(32641, 72, 3), (32768, 1000, 37), (33000, 520, 64),
+                                         (40000, 8, 17), (32768, 8192, 5)])
+def test_gemm_tiling_small_trees(dlh, V_high, d, M):
+    # Up to 64 draft rows a head of at least 256 tile pairs runs the GEMM
+    # tiling: hidden sizes that leave a partial last K step (72, 1000, 520)
+    # or a single chunk per row (8), a ragged last tile pair (33000, 40000),
+    # and the longest rows, whose staggered K loops wrap around d.
+    h, W, t2f = rand_case(900 + M, M, d, V_high, hscale=2.0)
+    check_case(dlh, h, W, t2f, 10)
 
 
 @pytest.mark.parametrize("V_high", [1, 10, 63, 64, 65, 1000, 4097])

@@ -48,8 +48,10 @@ def test_tiny_pipeline_draws_match_oracle(dlh):
     assert near <= 1
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 16, 33, 60, 64, 65, 130, 512])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 16, 33, 60, 64, 65, 130, 300, 384, 385, 512])
 def test_draws_match_oracle_gemv_and_mfma(dlh, M):
+    # Past 256 rows the draw runs on 96-row blocks up to 384 rows, on two
+    # groups of 256 rows beyond.
     h, W, t2f = rand_case(100 + M, M, 512, 3000, hscale=6.0)   # ragged V_high
     for off in (0, 1, 2**40 + 5):
         ids, probs = draw(dlh, h, W, t2f, 0xDEADBEEF12345, off)
