@@ -98,9 +98,9 @@ def median_us(fn, reps, torch):
 
 def head_kernels(M, V_high):
     """The kernels one draft-head call launches (the library's dispatch)."""
-    if M <= 2:
-        return "head_gemv_kernel"
     tile_pairs = (V_high + 127) // 128
+    if M == 1 or (M == 2 and tile_pairs < 256):
+        return "head_gemv_kernel"
     if M > 64 or tile_pairs >= 256:
         return "head_gemm_kernel + tree_merge_kernel"
     return ("head_mfma_kernel + tree_merge_kernel" if M <= 32 else

@@ -2,7 +2,8 @@
 // Implementation, Step 4; FR-Spec notes, key design), for gfx950. Every path
 // reads W_trim[V_high, d] from memory once; they differ in what else they
 // write, by number of draft rows M:
-//   * M <= 2, one kernel (head_gemv_kernel), no logit written to memory:
+//   * M = 1 (and M = 2 on a head of fewer than 512 tiles), one kernel
+//     (head_gemv_kernel), no logit written to memory:
 //     each wave computes whole rows (16-byte coalesced loads over d, packed
 //     bf16 dot products with fp32 accumulation against h held in
 //     registers, a DPP reduction); a tile's 64 logits go to LDS, where per
@@ -11,13 +12,13 @@
 //     workgroup that finishes last (atomic ticket) reads every partial once
 //     and merges them: the softmax partials in a fixed order, the keys by a
 //     threshold filter and a rank, so results do not depend on scheduling.
-//   * 3 <= M <= 512: a GEMM tiling on the matrix cores (head_gemm_kernel: one
+//   * 2 <= M <= 512: a GEMM tiling on the matrix cores (head_gemm_kernel: one
 //     8-wave workgroup per pair of W tiles over every draft row, both
 //     operands copied into an LDS ring), which writes each tile's fp32
 //     logits and softmax partials to the workspace, then one merge workgroup
 //     per draft row (tree_merge_kernel) that reads the partials and the
-//     logits of only the tiles that can hold a pick. Up to 64 rows on a
-//     head of fewer than 512 tiles (too few tile pairs to fill the chip) a
+//     logits of only the tiles that can hold a pick. From 3 to 64 rows on
+//     a head of fewer than 512 tiles (too few tile pairs to fill the chip) a
 //     skinny GEMM with one workgroup per tile (head_mfma_kernel; past 32
 //     rows h_pack_kernel first lays h out in operand order) takes its place.
 // Sampling (one draw per row) runs the same contraction kernels with a
@@ -34,9 +35,11 @@ namespace vt {
 namespace {
 
 constexpr int kGroups = 64;  // tile groups whose maxima bound the k-th key
-// Up to this many draft rows: GEMV path. From three rows on the MFMA path is
-// faster (measured: 49.8 us at 3 to 12 rows against 55.4 / 59.4 us for the
-// GEMV at 3 / 4 rows on the 4096 x 32768 head).
+// Up to this many draft rows the GEMV path can run. From three rows on the
+// MFMA path is faster (measured: 49.8 us at 3 to 12 rows against 55.4 /
+// 59.4 us for the GEMV at 3 / 4 rows on the 4096 x 32768 head), and at two
+// rows the GEMM tiling is where its tile pairs fill the chip (46.7 against
+// 47.0 us on that head, 41.0 against 42.0 us at d = 3584).
 constexpr int kGemvMaxRows = 2;
 
 struct HeadArgs {
@@ -1269,6 +1272,13 @@ __device__ __forceinline__ void gemm_epilogue(const HeadArgs &a, f32x4 (&acc)[4]
   const __amdgpu_buffer_rsrc_t zres = __builtin_amdgcn_make_buffer_rsrc(
       a.zbuf + (size_t)max(0, min(mw0, a.M - 1)) * a.zpitch + trow0, 0,
       zrows > 0 ? (int)(((size_t)zrows * a.zpitch - trow0) * 4) : 0, kBufferRsrcWord3);
+  auto store = [&](const f32x4 &v, int idx) {  // logits v at float index idx past zres
+    if (a.zstream)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), zres, idx * 4, 0,
+                                             kCpolNt);
+    else
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), zres, idx * 4, 0, 0);
+  };
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     const int m = mw0 + 16 * cb + r16;
@@ -1291,19 +1301,33 @@ __device__ __forceinline__ void gemm_epilogue(const HeadArgs &a, f32x4 (&acc)[4]
         if (trow0 + 16 * rb + 4 * g + i < a.V_high) S += __expf(acc[rb][cb][i] - mx);
     S += __shfl_xor(S, 16);
     S += __shfl_xor(S, 32);
-    if (m < a.M) {
+    // Logits out in whole 128-byte lines: for each pair of 16-row blocks
+    // (rb, rb + 1) lanes r16 and r16 ^ 8 swap one block (a DPP rotation by
+    // 8 within each row of 16 lanes), so that one store writes tile rows
+    // 32 pr .. 32 pr + 31 of draft rows 0..7 of the block (8 lanes per draft
+    // row) and the next those of draft rows 8..15. Storing each lane's own
+    // block instead (64 bytes per draft row and store) wrote 1.4 times the
+    // bytes past L2 (M = 60: 11.9 against 8.4 MB; M = 512: 98 against 71 MB)
+    // and took 4.7 us longer at M = 512.
+    const bool lo = r16 < 8;
+    const int rowA = lo ? r16 : r16 - 8, rowB = lo ? r16 + 8 : r16;
+    const int col = (lo ? 0 : 16) + 4 * g;
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const int off = ((16 * cb + r16) * a.zpitch + 16 * rb + 4 * g) * 4;
-        if (a.zstream)
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[rb][cb]), zres,
-                                                 off, 0, kCpolNt);
-        else
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[rb][cb]), zres,
-                                                 off, 0, 0);
-      }
-      if (g == 0) a.tile_ms[(size_t)m * a.tiles + tile] = pack_ms(mx, S);
+    for (int pr = 0; pr < 2; ++pr) {
+      const f32x4 a0 = acc[2 * pr][cb], a1 = acc[2 * pr + 1][cb];
+      const f32x4 send = lo ? a1 : a0;
+      // (__float_as_int, not __builtin_bit_cast: hipcc's bit_cast of a vector
+      // element send[i] reads element 0 whatever i is.)
+      f32x4 recv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        recv[i] = __int_as_float(
+            __builtin_amdgcn_mov_dpp(__float_as_int(send[i]), 0x128, 0xf, 0xf, false));
+      const f32x4 vA = lo ? a0 : recv, vB = lo ? recv : a1;
+      if (mw0 + 16 * cb + rowA < a.M) store(vA, (16 * cb + rowA) * a.zpitch + 32 * pr + col);
+      if (mw0 + 16 * cb + rowB < a.M) store(vB, (16 * cb + rowB) * a.zpitch + 32 * pr + col);
     }
+    if (m < a.M && g == 0) a.tile_ms[(size_t)m * a.tiles + tile] = pack_ms(mx, S);
   }
 }
 
@@ -1383,15 +1407,17 @@ __global__ __launch_bounds__(kGemmThreads) void head_gemm_kernel(HeadArgs a) {
   // that at any moment the rows in flight are spread over the width of d. In
   // step with one another they would all read the same 128-byte column of
   // 8 KiB-strided rows and crowd onto a few memory channels. The workgroups
-  // of one XCD (tile pairs p, p + 8, ...) start one step apart, so that
-  // their columns cover all of that XCD's L2 channels; every XCD uses the
-  // same offsets, and the two row groups of a tile pair (draws past 384
-  // rows) the same one. Measured on the 4096 x 32768 head against no stagger: M = 60
-  // 67.4 -> 46.2 us, M = 128 68.7 -> 56.0 us; starting tile pair p at step
-  // p mod steps instead (8 distinct offsets per XCD) gave 49.6 and 56.6 us,
-  // and shifting alternate XCDs by half of d 72.6 and 77.7 us.
+  // of one XCD (tile pairs p, p + 8, ...) start one step apart (three up to
+  // 32 draft rows), so that their columns cover all of that XCD's L2
+  // channels; every XCD uses the same offsets, and the two row groups of a
+  // tile pair (draws past 384 rows) the same one. Measured on the
+  // 4096 x 32768 head against no stagger: M = 60 67.4 -> 46.2 us, M = 128
+  // 68.7 -> 56.0 us; starting tile pair p at step p mod steps instead (8
+  // distinct offsets per XCD) gave 49.6 and 56.6 us, and shifting alternate
+  // XCDs by half of d 72.6 and 77.7 us. Three steps apart is 1 us faster up
+  // to 32 rows and 0.5 to 4 us slower from 60 rows on.
   const int steps = (c16 + kGemmKC - 1) / kGemmKC;
-  const int rot = (p / 8) % steps;
+  const int rot = ((a.M <= 32 ? 3 : 1) * (p / 8)) % steps;
   // K step s (the workgroup's s-th, step se of d) into ring stage s % S;
   // every step is issued, steps past the last (and chunks past d) as
   // out-of-range zero loads.
@@ -1572,6 +1598,12 @@ size_t head_zero_bytes() {
   return head_zero_prefix + (size_t)kGemvMaxRows * 2 * kGroups * 8;
 }
 
+// One draft row always takes the GEMV path; two rows take it on a head of
+// fewer than 256 tile pairs (on larger heads the GEMM tiling is faster).
+static bool gemv_path(int32_t M, int32_t tiles) {
+  return M == 1 || (M <= kGemvMaxRows && (tiles + 1) / 2 < kRingMinPairs);
+}
+
 HeadPlan head_plan(int32_t M, int32_t V_high, int32_t k) {
   // Fixed-offset prefix that every call leaves at zero: the ticket counter
   // (byte 0), the count of finished row mergers (byte 64), then the group
@@ -1584,7 +1616,7 @@ HeadPlan head_plan(int32_t M, int32_t V_high, int32_t k) {
   p.zero_bytes = off;
   // Tile keys: k per tile on the GEMV path; the MFMA path publishes one key
   // per tile, and only when sampling.
-  const bool mfma = M > kGemvMaxRows;
+  const bool mfma = !gemv_path(M, p.tiles);
   p.off_tile_keys = off;
   off += align_up((size_t)M * p.tiles * (mfma ? 1 : k) * 8, 256);
   p.off_tile_ms = off;
@@ -1641,11 +1673,12 @@ hipError_t launch_head_call(const uint16_t *h, int32_t M, int32_t d, const uint1
   a.zpitch = p.tiles * kTileRows;
   a.zstream = (size_t)M * p.tiles * kTileRows * 4 >= kZStreamBytes ? 1 : 0;
   a.ntt = (M + 15) / 16;
-  // Up to kGemvMaxRows rows: one GEMV pass with the merge in the same
-  // kernel. Up to 64 rows: the MFMA skinny GEMM over one tile per workgroup;
-  // more: the GEMM tiling of 128 x 128 blocks. Then one merge workgroup per
-  // draft row.
-  if (M <= kGemvMaxRows) return launch_gemv(a, stream);
+  // One draft row (two on a head of fewer than 256 tile pairs): one GEMV
+  // pass with the merge in the same kernel. Otherwise the GEMM tiling, one
+  // workgroup per tile pair, except up to 64 rows on a head too small for
+  // its tile pairs to fill the chip: there the 64-row MFMA kernel, one
+  // workgroup per tile. Then one merge workgroup per draft row.
+  if (gemv_path(M, p.tiles)) return launch_gemv(a, stream);
   if (M > kGroupRows || (p.tiles + 1) / 2 >= kRingMinPairs) return launch_gemm(a, stream);
   switch ((M + 15) / 16) {
     case 1: return launch_mfma<1>(a, stream);

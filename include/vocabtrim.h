@@ -193,17 +193,20 @@ int vt_gather_bias(const uint16_t *b, int32_t V, const int32_t *t2f, int32_t V_h
  *
  * What runs, by number of draft rows (W_trim is read from memory once in
  * every case):
- *   M <= 2      one kernel: a GEMV over W_trim whose workgroups rank each
+ *   M = 1, and M = 2 when V_high <= 32640
+ *               one kernel: a GEMV over W_trim whose workgroups rank each
  *               tile's logits on chip and publish per tile only the softmax
  *               partial and the tile's top-k keys; the last workgroups to
  *               finish merge them. No logit is written to memory.
- *   3 <= M <= 64   an MFMA skinny GEMM (one workgroup per tile; past 32 rows
- *               a small kernel first re-lays h out in operand order), then one
- *               merge workgroup per draft row. The fp32 logits of every tile
- *               go to the workspace and the merge reads back those of the
- *               few tiles that can hold a pick.
- *   M > 64      a GEMM-tiled MFMA kernel (128 x 128 blocks), logits to the
- *               workspace, then the same per-row merge.
+ *   otherwise   a GEMM-tiled MFMA kernel (one workgroup per 128 kept rows
+ *               over every draft row, both operands copied into an LDS
+ *               ring), then one merge workgroup per draft row. The fp32
+ *               logits of every tile of 64 kept rows go to the workspace and
+ *               the merge reads back those of the few tiles that can hold a
+ *               pick. With 3 <= M <= 64 and V_high <= 32640 an MFMA skinny
+ *               GEMM with one workgroup per tile (past 32 rows a small kernel
+ *               first re-lays h out in operand order) takes the GEMM-tiled
+ *               kernel's place.
  *
  * h         device, bf16[M, d], 16-byte aligned; 1 <= M <= VT_M_MAX
  * d         d % 8 == 0, 8 <= d <= VT_D_MAX
@@ -220,10 +223,11 @@ int vt_gather_bias(const uint16_t *b, int32_t V, const int32_t *t2f, int32_t V_h
  *           first 256 bytes hold the library's counters and status words
  *           (see vt_draft_head_status).
  * A merging workgroup waits, boundedly, for the other workgroups to arrive
- * (only with two draft rows). If that wait gives up (another process kept
- * workgroups from running for tens of milliseconds), the affected rows get
- * full_ids = -1 and NaN probabilities, and the workspace's error word is
- * raised; vt_draft_head_status reports and clears it. */
+ * (only on the GEMV path with two draft rows). If that wait gives up
+ * (another process kept workgroups from running for tens of milliseconds),
+ * the affected rows get full_ids = -1 and NaN probabilities, and the
+ * workspace's error word is raised; vt_draft_head_status reports and clears
+ * it. */
 size_t vt_draft_head_workspace_size(int32_t M, int32_t V_high, int32_t d,
                                     int32_t k);
 int vt_draft_head(const uint16_t *h, int32_t M, int32_t d,
