@@ -846,17 +846,21 @@ __device__ void row_merge(const HeadArgs &a, int m, MergeShared<WAVES> &sh, int3
   for (int base = 0; base < ne; base += kRound * NT) {
     float zv[kRound];
     int jv[kRound];
+    int32_t fv[kRound];
+    // The full ids are loaded beside the logits (one round trip to memory
+    // instead of a second one for the survivors).
 #pragma unroll
     for (int i = 0; i < kRound; ++i) {
       const int e = base + i * NT + tid;
       jv[i] = e < ne ? s_tiles[e / kTileRows] * kTileRows + e % kTileRows : V;
       zv[i] = jv[i] < V ? zr[jv[i]] : 0.f;
+      fv[i] = jv[i] < V ? fid_at(a, jv[i]) : 0;
     }
 #pragma unroll
     for (int i = 0; i < kRound; ++i)
       if (jv[i] < V && ord_from_f32(zv[i]) >= T) {
         const uint32_t pos = atomicAdd(&sh.cnt, 1u);
-        if (pos < (uint32_t)kCandCap) sh.cand[pos] = make_key(zv[i], fid_at(a, jv[i]));
+        if (pos < (uint32_t)kCandCap) sh.cand[pos] = make_key(zv[i], fv[i]);
       }
   }
   __syncthreads();
