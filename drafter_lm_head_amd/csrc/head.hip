@@ -120,19 +120,21 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // its own row's variates. Each lane reduces its draft row over its 16 tile
 // rows and two cross-lane steps combine the four lanes of a row. m0 is a
 // multiple of 16; every lane of the wave must call it.
-__device__ __forceinline__ void quad_draw_publish(const HeadArgs &a, int m0, int tile,
-                                                  int trow0, const f32x4 (&z)[4],
-                                                  const int32_t (&fid)[4][4]) {
+__device__ __forceinline__ uint32_t pick4(u32x4 w, int i) {
+  return i == 0 ? w[0] : i == 1 ? w[1] : i == 2 ? w[2] : w[3];
+}
+
+// The Gumbel variates of the quad-transposed draw: lane (g, r16) gets, for
+// each 16-row block rb and exchange k, the variate of draft row m0 + r16 at
+// tile row trow0 + 16 rb + 4 g + (r16 % 4 ^ k). Each quad lane draws the
+// Philox block of four draft rows at one of the quad's four tile rows, and
+// three exchanges within the quad (exchange k: send word r ^ k, receive from
+// lane r ^ k) hand every lane its own row's variates. They depend on nothing
+// but the seed, the offset and the indices, so a caller may draw them ahead.
+__device__ __forceinline__ void gumbel_quad(const HeadArgs &a, int m0, int trow0,
+                                            float (&gq)[4][4]) {
   const int lane = __lane_id(), g = lane >> 4, r16 = lane & 15, qr = r16 & 3;
   const int m = m0 + r16;
-  auto pick4 = [](u32x4 w, int i) -> uint32_t {
-    return i == 0 ? w[0] : i == 1 ? w[1] : i == 2 ? w[2] : w[3];
-  };
-  auto pickf = [](f32x4 w, int i) -> float {
-    return i == 0 ? w[0] : i == 1 ? w[1] : i == 2 ? w[2] : w[3];
-  };
-  uint64_t best = 0;
-  float zb = 0.f, mu = -INFINITY;
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     const u32x4 w = gumbel_words(a.seed_lo, a.seed_hi, a.off_lo, a.off_hi, (uint32_t)(m >> 2),
@@ -140,12 +142,43 @@ __device__ __forceinline__ void quad_draw_publish(const HeadArgs &a, int m0, int
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint32_t x = k == 0 ? pick4(w, qr) : (uint32_t)__shfl_xor((int)pick4(w, qr ^ k), k);
+      gq[rb][k] = gumbel_from_word(x);
+    }
+  }
+}
+
+// kPre: the variates come in gq (from gumbel_quad), else they are drawn here.
+template <bool kPre = false>
+__device__ __forceinline__ void quad_draw_publish(const HeadArgs &a, int m0, int tile,
+                                                  int trow0, const f32x4 (&z)[4],
+                                                  const int32_t (&fid)[4][4],
+                                                  const float (*gpre)[4] = nullptr) {
+  const int lane = __lane_id(), g = lane >> 4, r16 = lane & 15, qr = r16 & 3;
+  const int m = m0 + r16;
+  auto pickf = [](f32x4 w, int i) -> float {
+    return i == 0 ? w[0] : i == 1 ? w[1] : i == 2 ? w[2] : w[3];
+  };
+  float gq[4][4];
+  if constexpr (kPre) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) gq[rb][k] = gpre[rb][k];
+  } else {
+    gumbel_quad(a, m0, trow0, gq);
+  }
+  uint64_t best = 0;
+  float zb = 0.f, mu = -INFINITY;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
       const int i = qr ^ k;  // tile row (rb, i) of this variate
       const int32_t f = i == 0 ? fid[rb][0] : i == 1 ? fid[rb][1] : i == 2 ? fid[rb][2]
                                                                           : fid[rb][3];
       const float zv = pickf(z[rb], i);
       if (trow0 + 16 * rb + 4 * g + i < a.V_high) {
-        const uint64_t key = make_key(zv + gumbel_from_word(x), f);
+        const uint64_t key = make_key(zv + gq[rb][k], f);
         if (key > best) {
           best = key;
           zb = zv;
@@ -1230,24 +1263,37 @@ __device__ __forceinline__ int gemm_slot(int r, int c) { return r * kGemmKC + (c
 // The quad-transposed draw for column blocks I .. CB - 1 of a wave's
 // accumulators (blocks past M skipped), expanded at compile time so that
 // every accumulator index is static.
-template <int I, int CB>
+template <int I, int CB, bool kPre>
 __device__ __forceinline__ void draw_blocks(const HeadArgs &a, const f32x4 (&acc)[4][CB], int mw0,
-                                            int tile, int trow0, const int32_t (&fid)[4][4]) {
+                                            int tile, int trow0, const int32_t (&fid)[4][4],
+                                            const float (*gq)[4][4]) {
   if constexpr (I < CB) {
     if (mw0 + 16 * I < a.M) {  // uniform: the block has rows
       const f32x4 z[4] = {acc[0][I], acc[1][I], acc[2][I], acc[3][I]};
-      quad_draw_publish(a, mw0 + 16 * I, tile, trow0, z, fid);
+      quad_draw_publish<kPre>(a, mw0 + 16 * I, tile, trow0, z, fid, kPre ? gq[I] : nullptr);
     }
-    draw_blocks<I + 1, CB>(a, acc, mw0, tile, trow0, fid);
+    draw_blocks<I + 1, CB, kPre>(a, acc, mw0, tile, trow0, fid, gq);
   }
 }
+
+// Up to two 16-row blocks per wave the GEMM tiling draws its Gumbel
+// variates and loads the tile rows' full ids before its K loop, while the
+// ring fills (16 registers per block), instead of after it.
+template <int CB>
+constexpr bool kEarlyDraw = CB <= 2;
+template <int CB>
+struct EarlyDraw {
+  float gq[kEarlyDraw<CB> ? CB : 1][4][4];
+  int32_t fid[4][4];
+};
 
 // Epilogue of wave (wr, wc) of a GEMM-tiled workgroup over W tile pair p,
 // whose first draft row is mw0: lane (g, r16) holds, per (rb, cb), the
 // logits of tile rows 16 rb + 4 g .. + 3 for draft row mw0 + 16 cb + r16.
 template <int CB>
 __device__ __forceinline__ void gemm_epilogue(const HeadArgs &a, f32x4 (&acc)[4][CB], int p,
-                                              int wr, int mw0, int g, int r16) {
+                                              int wr, int mw0, int g, int r16,
+                                              const EarlyDraw<CB> &early) {
   const int tile = 2 * p + wr;
   const int trow0 = tile * kTileRows;
   // Sampling: the quad-transposed draw per 16-row column block (not
@@ -1261,12 +1307,15 @@ __device__ __forceinline__ void gemm_epilogue(const HeadArgs &a, f32x4 (&acc)[4]
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = trow0 + 16 * rb + 4 * g + i;
-        fid[rb][i] = row < a.V_high ? fid_at(a, row) : 0;
+        if constexpr (kEarlyDraw<CB>)
+          fid[rb][i] = early.fid[rb][i];
+        else
+          fid[rb][i] = row < a.V_high ? fid_at(a, row) : 0;
         if (a.bias && row < a.V_high)
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb) acc[rb][cb][i] += bf16_to_f32(a.bias[row]);
       }
-    draw_blocks<0, CB>(a, acc, mw0, tile, trow0, fid);
+    draw_blocks<0, CB, kEarlyDraw<CB>>(a, acc, mw0, tile, trow0, fid, early.gq);
     return;
   }
   if (tile >= a.tiles) return;
@@ -1450,6 +1499,22 @@ __global__ __launch_bounds__(kGemmThreads) void head_gemm_kernel(HeadArgs a) {
 
 #pragma unroll
   for (int s = 0; s < S - 1; ++s) issue(s);
+  EarlyDraw<CB> early;
+  if constexpr (kEarlyDraw<CB>) {
+    if (a.sample) {
+      const int trow0 = (2 * p + wr) * kTileRows;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+        gumbel_quad(a, mrow0 + 16 * CB * wc + 16 * cb, trow0, early.gq[cb]);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = trow0 + 16 * rb + 4 * g + i;
+          early.fid[rb][i] = row < a.V_high ? fid_at(a, row) : 0;
+        }
+    }
+  }
 #pragma unroll 1
   for (int s = 0; s < steps; ++s) {
     // This wave's loads of step s have landed (the S - 2 later steps may
@@ -1482,7 +1547,7 @@ __global__ __launch_bounds__(kGemmThreads) void head_gemm_kernel(HeadArgs a) {
   }
   // No load into this workgroup's LDS may outlive it.
   wait_vmcnt<0>();
-  gemm_epilogue<CB>(a, acc, p, wr, mrow0 + 16 * CB * wc, g, r16);
+  gemm_epilogue<CB>(a, acc, p, wr, mrow0 + 16 * CB * wc, g, r16, early);
 }
 
 template <int CB, int S>
