@@ -100,9 +100,12 @@ def test_biased_head_full_size(dlh, M):
     check_picks(ids.cpu().numpy(), probs.cpu().numpy(), z_o, t2f, w.k, ids_o)
 
 
-@pytest.mark.parametrize("M", [2, 9, 70])
-def test_biased_draws_match_oracle(dlh, M):
-    h, W, b, t2f = biased_case(300 + M, M, 256, 2000, bias_std=2.0)
+@pytest.mark.parametrize("M,V_high", [(2, 2000), (9, 2000), (70, 2000), (2, 33000), (40, 33000)])
+def test_biased_draws_match_oracle(dlh, M, V_high):
+    # Small heads: GEMV (two rows), 64-row kernel, GEMM tiling; heads of 256 or
+    # more tile pairs: the GEMM tiling with its variates drawn before the K
+    # loop, here with a ragged last tile pair.
+    h, W, b, t2f = biased_case(300 + M, M, 256, V_high, bias_std=2.0)
     near = 0
     for off in range(4):
         ids, probs = dlh.vt_draft_sample_bias(to_dev_bf16(h), to_dev_bf16(W), to_dev_bf16(b),

@@ -44,9 +44,12 @@ def capture(fn):
     return g
 
 
-@pytest.mark.parametrize("M", [1, 8, 60])
-def test_draft_head_graph_replays_match_eager(dlh, M):
-    V_high, d, k = 5000, 512, 10
+@pytest.mark.parametrize("M,V_high,d", [(1, 5000, 512), (8, 5000, 512), (60, 5000, 512),
+                                         (2, 32768, 256), (60, 32768, 256)])
+def test_draft_head_graph_replays_match_eager(dlh, M, V_high, d):
+    # Small heads: the GEMV and the 64-row kernel; 256 tile pairs: the GEMM
+    # tiling on its LDS ring.
+    k = 10
     h, W, t2f = case(M, M, d, V_high)
     h2, _, _ = case(M + 100, M, d, V_high)
     ws = torch.zeros(dlh.vt_draft_head_workspace_size(M, V_high, d, k), dtype=torch.uint8,
@@ -70,9 +73,9 @@ def test_draft_head_graph_replays_match_eager(dlh, M):
         assert (ids.cpu().numpy().tobytes(), probs.cpu().numpy().tobytes()) == ref, rep
 
 
-@pytest.mark.parametrize("M", [1, 9])
-def test_draft_sample_graph_replays_match_eager(dlh, M):
-    V_high, d = 3000, 256
+@pytest.mark.parametrize("M,V_high", [(1, 3000), (9, 3000), (40, 32768)])
+def test_draft_sample_graph_replays_match_eager(dlh, M, V_high):
+    d = 256
     h, W, t2f = case(7 + M, M, d, V_high)
     ws = torch.zeros(dlh.vt_draft_head_workspace_size(M, V_high, d, 1), dtype=torch.uint8,
                      device=DEV)
