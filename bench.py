@@ -98,13 +98,12 @@ def median_us(fn, reps, torch):
 
 def head_kernels(M, V_high):
     """The kernels one draft-head call launches (the library's dispatch)."""
-    tile_pairs = (V_high + 127) // 128
-    if M == 1 or (M == 2 and tile_pairs < 256):
+    tiles = (V_high + 63) // 64
+    if M == 1 or (M == 2 and (tiles + 1) // 2 < 256):
         return "head_gemv_kernel"
-    if M > 64 or tile_pairs >= 256:
+    if M > 32 or tiles >= 256:
         return "head_gemm_kernel + tree_merge_kernel"
-    return ("head_mfma_kernel + tree_merge_kernel" if M <= 32 else
-            "h_pack_kernel + head_mfma_kernel + tree_merge_kernel")
+    return "head_mfma_kernel + tree_merge_kernel"
 
 
 def recorded_traffic():

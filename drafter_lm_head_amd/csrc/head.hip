@@ -1247,10 +1247,7 @@ __global__ __launch_bounds__(WAVES *kWave) void tree_merge_kernel(HeadArgs a) {
 // and draft rows 16 CB wc .. over the whole of d, so it ends with final
 // sums: logits and the (draft row, tile) softmax partials (or the tile's
 // draws) go out as on the 64-row path and the same row merges follow.
-constexpr int kGemmRows = 128;                  // W rows per workgroup
 constexpr int kGemmKC = 8;                      // 16-byte chunks per row and K step
-constexpr int kGemmWaves = 8;
-constexpr int kGemmThreads = kGemmWaves * kWave;
 
 // Slot of 16-byte chunk c of staged row r (rows of 8 chunks). The chunk index
 // is XOR-swizzled by the row's low three bits: the operand reads (16 rows at
@@ -1291,10 +1288,9 @@ struct EarlyDraw {
 // whose first draft row is mw0: lane (g, r16) holds, per (rb, cb), the
 // logits of tile rows 16 rb + 4 g .. + 3 for draft row mw0 + 16 cb + r16.
 template <int CB>
-__device__ __forceinline__ void gemm_epilogue(const HeadArgs &a, f32x4 (&acc)[4][CB], int p,
-                                              int wr, int mw0, int g, int r16,
+__device__ __forceinline__ void gemm_epilogue(const HeadArgs &a, f32x4 (&acc)[4][CB], int tile,
+                                              int mw0, int g, int r16,
                                               const EarlyDraw<CB> &early) {
-  const int tile = 2 * p + wr;
   const int trow0 = tile * kTileRows;
   // Sampling: the quad-transposed draw per 16-row column block (not
   // compiled for 8 blocks per wave, whose registers it would overflow; the
@@ -1384,9 +1380,13 @@ __device__ __forceinline__ void gemm_epilogue(const HeadArgs &a, f32x4 (&acc)[4]
   }
 }
 
-// Up to 64 draft rows the GEMM tiling takes over from the 64-row kernel once
-// its workgroups (one per pair of W tiles) fill the chip's 256 CUs; with
-// fewer the 64-row kernel's one workgroup per tile keeps more CUs streaming.
+// A workgroup of the GEMM tiling covers a pair of W tiles once there are
+// enough pairs to give each of the 256 CUs one (heads of 512 tiles or more),
+// else a single tile (4 waves): up to 64 draft rows such workgroups also fit
+// two to a CU, past 64 rows one, so past 64 rows the single-tile form is
+// taken only up to 256 tiles. Up to 32 rows on heads of fewer than 256 tiles
+// the 64-row kernel (one workgroup per tile, its four waves streaming their
+// own quarters of d with no barrier per step) is faster still.
 constexpr int kRingMinPairs = 256;
 
 // Both operands are copied from memory straight into LDS (buffer loads with
@@ -1398,14 +1398,15 @@ constexpr int kRingMinPairs = 256;
 // reads chunk (l % 8) ^ (l / 8) of that row. Chunks past d and rows past
 // V_high or M are addressed outside the buffer ranges, which the hardware
 // turns into zeros in LDS.
-template <int CB, int S>
+template <int CB, int S, int TPW>
 struct GemmRing {
+  static constexpr int kRows = TPW * kTileRows;        // W rows per workgroup
+  static constexpr int kWaves = 4 * TPW;
   static constexpr int kDraftRows = 4 * 16 * CB;
-  static constexpr int kSlots = (kGemmRows + kDraftRows) * kGemmKC;  // per stage
-  static constexpr int kLoads = (kGemmRows + kDraftRows) / 8 / kGemmWaves;
-  static constexpr int kWLoads = kGemmRows / 8 / kGemmWaves;
-  static_assert(kLoads * 8 * kGemmWaves == kGemmRows + kDraftRows &&
-                    kWLoads * 8 * kGemmWaves == kGemmRows,
+  static constexpr int kSlots = (kRows + kDraftRows) * kGemmKC;  // per stage
+  static constexpr int kLoads = (kRows + kDraftRows) / 8 / kWaves;
+  static constexpr int kWLoads = kRows / 8 / kWaves;
+  static_assert(kLoads * 8 * kWaves == kRows + kDraftRows && kWLoads * 8 * kWaves == kRows,
                 "every wave issues whole 8-row blocks of each operand");
   static_assert(S >= 2 && (S - 1) * kLoads <= 63, "the in-flight loads must fit vmcnt");
   static_assert(S * kSlots * 16 <= 160 * 1024, "the ring must fit the LDS");
@@ -1422,16 +1423,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 // kShared: more than one group of draft rows, so each pair of W tiles is
 // read by two workgroups of one XCD (plain loads keep it in L2 for the
 // other); otherwise W is streamed once, non-temporally.
-template <bool kShared, int CB, int S>
-__global__ __launch_bounds__(kGemmThreads) void head_gemm_kernel(HeadArgs a) {
-  using Ring = GemmRing<CB, S>;
-  constexpr int kDR = Ring::kDraftRows, kWaves = kGemmWaves;
+template <bool kShared, int CB, int S, int TPW>
+__global__ __launch_bounds__(4 * TPW * kWave) void head_gemm_kernel(HeadArgs a) {
+  using Ring = GemmRing<CB, S, TPW>;
+  constexpr int kDR = Ring::kDraftRows, kWaves = Ring::kWaves, kRows = Ring::kRows;
   constexpr int kLoads = Ring::kLoads, kWLoads = Ring::kWLoads, kSlots = Ring::kSlots;
   __shared__ u32x4 ring[S * kSlots];
   // The wave index is uniform (the LDS address of a load must be).
   const int tid = threadIdx.x, lane = __lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int tpairs = (a.tiles + 1) / 2, gpairs = (a.M + kDR - 1) / kDR;
+  const int tpairs = (a.tiles + TPW - 1) / TPW, gpairs = (a.M + kDR - 1) / kDR;
   // Workgroup -> (tile pair p, draft-row group q); past 384 draft rows (draws
   // only) the groups of one tile pair take consecutive slots of one XCD, so
   // that the later one finds the W rows in that XCD's L2.
@@ -1439,10 +1440,10 @@ __global__ __launch_bounds__(kGemmThreads) void head_gemm_kernel(HeadArgs a) {
   const int q = slot % gpairs, p = xcd + 8 * (slot / gpairs);
   if (p >= tpairs) return;
   const int c16 = a.c16;
-  const int wrow0 = p * kGemmRows, mrow0 = q * kDR;
+  const int wrow0 = p * kRows, mrow0 = q * kDR;
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<u32x4 *>(a.W + (size_t)wrow0 * c16), 0,
-      min(kGemmRows, a.V_high - wrow0) * c16 * 16, kBufferRsrcWord3);
+      min(kRows, a.V_high - wrow0) * c16 * 16, kBufferRsrcWord3);
   const __amdgpu_buffer_rsrc_t hres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<u32x4 *>(a.h + (size_t)mrow0 * c16), 0,
       min(kDR, a.M - mrow0) * c16 * 16, kBufferRsrcWord3);
@@ -1453,7 +1454,7 @@ __global__ __launch_bounds__(kGemmThreads) void head_gemm_kernel(HeadArgs a) {
 #pragma unroll
   for (int j = 0; j < kLoads; ++j) {
     const int blk = wave + kWaves * j;
-    const int row = 8 * (j < kWLoads ? blk : blk - kGemmRows / 8) + lrow;
+    const int row = 8 * (j < kWLoads ? blk : blk - kRows / 8) + lrow;
     voff[j] = (uint32_t)(row * c16 + lchunk) * 16u;
   }
   // Workgroups start their K loop at staggered steps and wrap around, so
@@ -1489,7 +1490,7 @@ __global__ __launch_bounds__(kGemmThreads) void head_gemm_kernel(HeadArgs a) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(hres, dst, 16, off, 0, 0, 0);
     }
   };
-  const int wr = wave & 1, wc = wave >> 1;
+  const int wr = TPW == 2 ? wave & 1 : 0, wc = TPW == 2 ? wave >> 1 : wave;
   const int g = lane >> 4, r16 = lane & 15;
   f32x4 acc[4][CB];
 #pragma unroll
@@ -1502,7 +1503,7 @@ __global__ __launch_bounds__(kGemmThreads) void head_gemm_kernel(HeadArgs a) {
   EarlyDraw<CB> early;
   if constexpr (kEarlyDraw<CB>) {
     if (a.sample) {
-      const int trow0 = (2 * p + wr) * kTileRows;
+      const int trow0 = (TPW * p + wr) * kTileRows;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
         gumbel_quad(a, mrow0 + 16 * CB * wc + 16 * cb, trow0, early.gq[cb]);
@@ -1536,7 +1537,7 @@ __global__ __launch_bounds__(kGemmThreads) void head_gemm_kernel(HeadArgs a) {
       for (int rb = 0; rb < 4; ++rb) av[rb] = st[gemm_slot(64 * wr + 16 * rb + r16, cl)];
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        const u32x4 bv = st[kGemmRows * kGemmKC + gemm_slot(16 * CB * wc + 16 * cb + r16, cl)];
+        const u32x4 bv = st[kRows * kGemmKC + gemm_slot(16 * CB * wc + 16 * cb + r16, cl)];
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb)
           acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -1547,18 +1548,19 @@ __global__ __launch_bounds__(kGemmThreads) void head_gemm_kernel(HeadArgs a) {
   }
   // No load into this workgroup's LDS may outlive it.
   wait_vmcnt<0>();
-  gemm_epilogue<CB>(a, acc, p, wr, mrow0 + 16 * CB * wc, g, r16, early);
+  gemm_epilogue<CB>(a, acc, TPW * p + wr, mrow0 + 16 * CB * wc, g, r16, early);
 }
 
-template <int CB, int S>
+template <int CB, int S, int TPW = 2>
 hipError_t launch_gemm_shape(const HeadArgs &a, hipStream_t stream) {
-  const int tpairs = (a.tiles + 1) / 2;
-  const int gpairs = (a.M + GemmRing<CB, S>::kDraftRows - 1) / GemmRing<CB, S>::kDraftRows;
-  const dim3 grid(8 * ((tpairs + 7) / 8) * gpairs), block(kGemmThreads);
+  using Ring = GemmRing<CB, S, TPW>;
+  const int units = (a.tiles + TPW - 1) / TPW;
+  const int gpairs = (a.M + Ring::kDraftRows - 1) / Ring::kDraftRows;
+  const dim3 grid(8 * ((units + 7) / 8) * gpairs), block(Ring::kWaves * kWave);
   if (gpairs > 1)
-    hipLaunchKernelGGL((head_gemm_kernel<true, CB, S>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((head_gemm_kernel<true, CB, S, TPW>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((head_gemm_kernel<false, CB, S>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((head_gemm_kernel<false, CB, S, TPW>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -1569,10 +1571,12 @@ hipError_t launch_gemm_shape(const HeadArgs &a, hipStream_t stream) {
 // fit the registers next to 8 column blocks).
 hipError_t launch_gemm(const HeadArgs &a, hipStream_t stream) {
   hipError_t e;
+  const bool pairs = (a.tiles + 1) / 2 >= kRingMinPairs;
   if (a.M <= 64)
-    e = launch_gemm_shape<1, 4>(a, stream);
+    e = pairs ? launch_gemm_shape<1, 4, 2>(a, stream) : launch_gemm_shape<1, 4, 1>(a, stream);
   else if (a.M <= 128)
-    e = launch_gemm_shape<2, 4>(a, stream);
+    e = a.tiles > kRingMinPairs ? launch_gemm_shape<2, 4, 2>(a, stream)
+                                : launch_gemm_shape<2, 4, 1>(a, stream);
   else if (a.M <= 256 || (a.sample && a.M > 384))
     e = launch_gemm_shape<4, 3>(a, stream);
   else if (a.M <= 384)
@@ -1743,12 +1747,11 @@ hipError_t launch_head_call(const uint16_t *h, int32_t M, int32_t d, const uint1
   a.zstream = (size_t)M * p.tiles * kTileRows * 4 >= kZStreamBytes ? 1 : 0;
   a.ntt = (M + 15) / 16;
   // One draft row (two on a head of fewer than 256 tile pairs): one GEMV
-  // pass with the merge in the same kernel. Otherwise the GEMM tiling, one
-  // workgroup per tile pair, except up to 64 rows on a head too small for
-  // its tile pairs to fill the chip: there the 64-row MFMA kernel, one
-  // workgroup per tile. Then one merge workgroup per draft row.
+  // pass with the merge in the same kernel. Up to 32 rows on a head of
+  // fewer than 256 tiles: the 64-row MFMA kernel, one workgroup per tile.
+  // Otherwise the GEMM tiling. Then one merge workgroup per draft row.
   if (gemv_path(M, p.tiles)) return launch_gemv(a, stream);
-  if (M > kGroupRows || (p.tiles + 1) / 2 >= kRingMinPairs) return launch_gemm(a, stream);
+  if (M > 32 || p.tiles >= kRingMinPairs) return launch_gemm(a, stream);
   switch ((M + 15) / 16) {
     case 1: return launch_mfma<1>(a, stream);
     case 2: return launch_mfma<2>(a, stream);
