@@ -12,15 +12,15 @@
 //     workgroup that finishes last (atomic ticket) reads every partial once
 //     and merges them: the softmax partials in a fixed order, the keys by a
 //     threshold filter and a rank, so results do not depend on scheduling.
-//   * 2 <= M <= 512: a GEMM tiling on the matrix cores (head_gemm_kernel: one
-//     8-wave workgroup per pair of W tiles over every draft row, both
-//     operands copied into an LDS ring), which writes each tile's fp32
-//     logits and softmax partials to the workspace, then one merge workgroup
-//     per draft row (tree_merge_kernel) that reads the partials and the
-//     logits of only the tiles that can hold a pick. From 3 to 64 rows on
-//     a head of fewer than 512 tiles (too few tile pairs to fill the chip) a
-//     skinny GEMM with one workgroup per tile (head_mfma_kernel; past 32
-//     rows h_pack_kernel first lays h out in operand order) takes its place.
+//   * 2 <= M <= 512: a GEMM tiling on the matrix cores (head_gemm_kernel:
+//     one workgroup per pair of W tiles, or per tile on heads of fewer than
+//     512 tiles, over every draft row, both operands copied into an LDS
+//     ring), which writes each tile's fp32 logits and softmax partials to
+//     the workspace, then one merge workgroup per draft row
+//     (tree_merge_kernel) that reads the partials and the logits of only the
+//     tiles that can hold a pick. From 3 to 32 rows on a head of fewer than
+//     256 tiles a skinny GEMM with one workgroup per tile whose waves stream
+//     their own quarters of d (head_mfma_kernel) takes its place.
 // Sampling (one draw per row) runs the same contraction kernels with a
 // per-tile draw in place of the logits. Up to M of about 312 the head is
 // bound by HBM bandwidth: it moves 2 * V_high * d bytes of W_trim for
@@ -57,7 +57,6 @@ struct HeadArgs {
   int32_t *full_ids;     // [M][k]
   float *probs;          // [M][k]
   float *logits;         // [M][V_high], logits-only variant
-  const u32x4 *hp;       // h in MFMA B-operand order (MFMA path)
   uint32_t *merged;      // GEMV path, two draft rows: finished row mergers (zero between calls)
   int32_t zstream;       // MFMA path: logits to the workspace with streaming stores
   // Sampling mode (k = 1): the pick is the largest z + Gumbel(seed, offset).
@@ -67,7 +66,6 @@ struct HeadArgs {
   const uint16_t *bias;  // bf16[V_high] added to every logit, or nullptr
   int32_t remap;         // 1: keys carry t2f[j] (full ids); 0: the trimmed index j
   uint32_t *status;      // the workspace's fixed words (error, hold, spin limit)
-  int32_t ntt;           // MFMA path: 16-row column blocks over all M rows
   float *zbuf;           // MFMA path, top-k mode: logits [M][zpitch]
   int32_t zpitch;        // tiles * kTileRows floats
 };
@@ -974,7 +972,7 @@ constexpr int kMfmaWaves = 4;
 constexpr size_t kZStreamBytes = 6u << 20;
 constexpr int kCpolNt = 2;                     // cache policy: non-temporal (streaming)
 constexpr int kBufferRsrcWord3 = 0x00020000;   // raw 32-bit data, no swizzle
-constexpr int kGroupRows = 64;  // draft rows per MFMA workgroup (4 column blocks)
+constexpr int kGroupRows = 32;  // draft rows of the 64-row kernel (2 column blocks)
 
 // W is staged through wave-private LDS: the operand layout (16 rows x 64
 // bytes per load) is slow to fetch from HBM directly, so each load
@@ -987,27 +985,9 @@ constexpr int kStagePitch = kStageChunks + 2;         // row pitch in chunks
 constexpr int kStageSize = kTileRows * kStagePitch;   // chunks per wave
 constexpr int kPartPitch = kTileRows + 4;             // floats per partial-sum row
 
-// h re-laid out in B-operand order, so that each B load of the MFMA loop
-// reads 1 KiB contiguous: hp[(s * NT + cb) * 64 + l] = the 16-byte chunk
-// 4 s + l / 16 of draft row 16 cb + l % 16 (zero past M or d).
-__global__ __launch_bounds__(kWave) void h_pack_kernel(const u32x4 *__restrict__ h, int M,
-                                                       int c16, int NT, u32x4 *__restrict__ hp) {
-  const int s = blockIdx.x / NT, cb = blockIdx.x % NT, l = threadIdx.x;
-  const int row = cb * 16 + (l & 15), ch = 4 * s + (l >> 4);
-  hp[(size_t)blockIdx.x * kWave + l] =
-      (row < M && ch < c16) ? h[(size_t)row * c16 + ch] : u32x4{0, 0, 0, 0};
-}
-
-// With one or two 16-row column blocks the B operands are read straight
-// from h (16 rows x 64 bytes per load) and the packing kernel is skipped;
-// with more blocks the scattered reads cost more than the extra kernel.
-template <int NT>
-constexpr bool kDirectH = NT <= 2;
-
-
-// Up to 64 draft rows, one workgroup per tile; each W tile is read once and
-// streams past the caches (non-temporal loads; plain ones cost 4.5 us at
-// M = 60).
+// Up to 32 draft rows on small heads, one workgroup per tile; each W tile is
+// read once and streams past the caches (non-temporal loads; plain ones cost
+// 4.5 us at M = 60 when this kernel also served 60 rows).
 template <int NT>
 __global__ __launch_bounds__(kMfmaWaves *kWave) __attribute__((amdgpu_waves_per_eu(2)))
 void head_mfma_kernel(HeadArgs a) {
@@ -1067,19 +1047,13 @@ void head_mfma_kernel(HeadArgs a) {
     u32x4 bv[kStageChunks / 4][NT];
 #pragma unroll
     for (int t = 0; t < kStageChunks / 4; ++t) {
+      // The B operands straight from h (16 rows x 64 bytes per load).
       const bool ok = base + 4 * t + g < c_hi;
-      if (kDirectH<NT>) {
-        const int ch = base + 4 * t + g;
+      const int ch = base + 4 * t + g;
 #pragma unroll
-        for (int cb = 0; cb < NT; ++cb) {
-          const int row = cb * 16 + r16;
-          bv[t][cb] = (ok && row < M) ? a.h[(size_t)row * c16 + ch] : u32x4{0, 0, 0, 0};
-        }
-      } else {
-        const u32x4 *hs = a.hp + (size_t)((base / 4 + t) * a.ntt) * kWave + lane;
-#pragma unroll
-        for (int cb = 0; cb < NT; ++cb)
-          bv[t][cb] = (ok && cb < a.ntt) ? hs[cb * kWave] : u32x4{0, 0, 0, 0};
+      for (int cb = 0; cb < NT; ++cb) {
+        const int row = cb * 16 + r16;
+        bv[t][cb] = (ok && row < M) ? a.h[(size_t)row * c16 + ch] : u32x4{0, 0, 0, 0};
       }
     }
     if constexpr (decltype(prefetch)::value) load_stage(v, base + kStageChunks);
@@ -1594,13 +1568,7 @@ hipError_t launch_gemm(const HeadArgs &a, hipStream_t stream) {
 
 template <int NT>
 hipError_t launch_mfma(const HeadArgs &a, hipStream_t stream) {
-  const int steps = (a.c16 + 3) / 4;
-  if (!kDirectH<NT>) {
-    hipLaunchKernelGGL(h_pack_kernel, dim3(steps * a.ntt), dim3(kWave), 0, stream, a.h, a.M,
-                       a.c16, a.ntt, const_cast<u32x4 *>(a.hp));
-    hipError_t e0 = hipGetLastError();
-    if (e0 != hipSuccess) return e0;
-  }
+  static_assert(NT == 1 || NT == 2, "up to 32 draft rows");
   hipLaunchKernelGGL((head_mfma_kernel<NT>), dim3(a.tiles), dim3(kMfmaWaves * kWave), 0,
                      stream, a);
   hipError_t e = hipGetLastError();
@@ -1661,8 +1629,6 @@ hipError_t launch_gemv(const HeadArgs &a, hipStream_t stream) {
 
 }  // namespace
 
-static_assert(kDirectH<2> && !kDirectH<3>, "packed h is allocated for more than 32 rows");
-
 // Counters and status words (256 bytes), then the GEMV path's group maxima.
 constexpr size_t head_zero_prefix = 256;
 static_assert(kWsSpinLimit + 4 <= head_zero_prefix, "status words inside the prefix");
@@ -1696,10 +1662,6 @@ HeadPlan head_plan(int32_t M, int32_t V_high, int32_t k) {
   off += align_up((size_t)M * p.tiles * 8, 256);
   p.off_tile_z = off;  // sampling mode: z of each tile's drawn row
   off += align_up((size_t)M * p.tiles * 8, 256);
-  p.off_hpack = off;  // 64-row MFMA path past 32 rows: h in B-operand order, 16 * NT rows x d
-  off += (M > 32 && M <= kGroupRows)
-             ? align_up((size_t)((M + 15) / 16) * 16 * (size_t)VT_D_MAX * 2, 256)
-             : 0;
   p.off_zbuf = off;  // MFMA path, top-k mode: logits [M][tiles * kTileRows] fp32
   off += mfma ? align_up((size_t)M * p.tiles * kTileRows * 4, 256) : 0;
   p.bytes = off;
@@ -1731,7 +1693,6 @@ hipError_t launch_head_call(const uint16_t *h, int32_t M, int32_t d, const uint1
   a.group_max = reinterpret_cast<uint64_t *>(base + p.off_group);
   a.group_kth = a.group_max + (size_t)kGemvMaxRows * kGroups;
   a.tiles_per_group = (p.tiles + kGroups - 1) / kGroups;
-  a.hp = reinterpret_cast<const u32x4 *>(base + p.off_hpack);
   a.M = M;
   a.h = reinterpret_cast<const u32x4 *>(h);
   a.full_ids = full_ids;
@@ -1745,19 +1706,13 @@ hipError_t launch_head_call(const uint16_t *h, int32_t M, int32_t d, const uint1
   a.zbuf = reinterpret_cast<float *>(base + p.off_zbuf);
   a.zpitch = p.tiles * kTileRows;
   a.zstream = (size_t)M * p.tiles * kTileRows * 4 >= kZStreamBytes ? 1 : 0;
-  a.ntt = (M + 15) / 16;
   // One draft row (two on a head of fewer than 256 tile pairs): one GEMV
   // pass with the merge in the same kernel. Up to 32 rows on a head of
   // fewer than 256 tiles: the 64-row MFMA kernel, one workgroup per tile.
   // Otherwise the GEMM tiling. Then one merge workgroup per draft row.
   if (gemv_path(M, p.tiles)) return launch_gemv(a, stream);
-  if (M > 32 || p.tiles >= kRingMinPairs) return launch_gemm(a, stream);
-  switch ((M + 15) / 16) {
-    case 1: return launch_mfma<1>(a, stream);
-    case 2: return launch_mfma<2>(a, stream);
-    case 3: return launch_mfma<3>(a, stream);
-    default: return launch_mfma<4>(a, stream);
-  }
+  if (M > kGroupRows || p.tiles >= kRingMinPairs) return launch_gemm(a, stream);
+  return M <= 16 ? launch_mfma<1>(a, stream) : launch_mfma<2>(a, stream);
 }
 }  // namespace
 

@@ -52,7 +52,7 @@ constexpr size_t kWsHold = VT_WS_HOLD_OFFSET;          // uint32, see vocabtrim.
 constexpr size_t kWsSpinLimit = VT_WS_SPIN_LIMIT_OFFSET;  // uint32, see vocabtrim.h
 struct HeadPlan {
   int32_t tiles;
-  size_t off_group, zero_bytes, off_tile_keys, off_tile_ms, off_tile_z, off_hpack, off_zbuf;
+  size_t off_group, zero_bytes, off_tile_keys, off_tile_ms, off_tile_z, off_zbuf;
   size_t bytes;
 };
 HeadPlan head_plan(int32_t M, int32_t V_high, int32_t k);
