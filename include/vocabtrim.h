@@ -198,15 +198,14 @@ int vt_gather_bias(const uint16_t *b, int32_t V, const int32_t *t2f, int32_t V_h
  *               tile's logits on chip and publish per tile only the softmax
  *               partial and the tile's top-k keys; the last workgroups to
  *               finish merge them. No logit is written to memory.
- *   otherwise   a GEMM-tiled MFMA kernel (one workgroup per 128 kept rows
- *               over every draft row, both operands copied into an LDS
- *               ring), then one merge workgroup per draft row. The fp32
- *               logits of every tile of 64 kept rows go to the workspace and
- *               the merge reads back those of the few tiles that can hold a
- *               pick. With 3 <= M <= 64 and V_high <= 32640 an MFMA skinny
- *               GEMM with one workgroup per tile (past 32 rows a small kernel
- *               first re-lays h out in operand order) takes the GEMM-tiled
- *               kernel's place.
+ *   otherwise   a GEMM-tiled MFMA kernel (one workgroup per 128 kept rows,
+ *               or per 64 when V_high <= 32640, over every draft row, both
+ *               operands copied into an LDS ring), then one merge workgroup
+ *               per draft row. The fp32 logits of every tile of 64 kept rows
+ *               go to the workspace and the merge reads back those of the
+ *               few tiles that can hold a pick. With 3 <= M <= 32 and
+ *               V_high <= 16320 an MFMA skinny GEMM with one workgroup per
+ *               tile takes the GEMM-tiled kernel's place.
  *
  * h         device, bf16[M, d], 16-byte aligned; 1 <= M <= VT_M_MAX
  * d         d % 8 == 0, 8 <= d <= VT_D_MAX

@@ -79,8 +79,8 @@ def test_draft_tree_rows(dlh, M):
 def test_draft_tree_edges(dlh, V_high, d, k, M):
     # Ragged tiles and row groups: a last tile of one row, a last group of
     # two (M = 130) or one (M = 193) draft rows; the longest rows (d = 8192)
-    # on the 64-row and GEMM-tiled kernels, and one 16-byte chunk per row
-    # (d = 8) with packed h.
+    # on the GEMM tiling's single-tile and tile-pair workgroups, and one
+    # 16-byte chunk per row (d = 8).
     h, W, t2f = rand_case(300 + V_high, M, d, V_high, hscale=2.0)
     check_case(dlh, h, W, t2f, min(k, V_high))
 
