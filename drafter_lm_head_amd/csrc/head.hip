@@ -220,6 +220,7 @@ struct alignas(16) MergeShared {
   alignas(16) uint64_t cand[kCandCap];       // survivors of the threshold
   alignas(16) uint64_t sc[2][kWave];         // rank inputs / outputs
   uint32_t prank[4][4][kWave];               // partial ranks
+  uint32_t gm[WAVES][kWave];                 // per-wave maxima of the tile groups
   unsigned long long kmax;
   uint32_t cnt;
   float f[WAVES], f2[WAVES], zw[WAVES];
@@ -803,8 +804,7 @@ __device__ void row_merge(const HeadArgs &a, int m, MergeShared<WAVES> &sh, int3
                           uint32_t &s_ntiles) {
   constexpr int NT = WAVES * kWave;
   constexpr int kTpt = (kMaxTiles + NT - 1) / NT;  // tiles per thread
-  constexpr int GS = NT / kWave;                   // threads per tile group
-  static_assert((GS & (GS - 1)) == 0 && GS <= kWave, "group of threads within a wave");
+  static_assert(NT % kGroups == 0, "a thread's tiles share its group");
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
   const int k = a.k, V = a.V_high, tiles = a.tiles;
   const uint64_t *ms = a.tile_ms + (size_t)m * tiles;
@@ -824,13 +824,13 @@ __device__ void row_merge(const HeadArgs &a, int m, MergeShared<WAVES> &sh, int3
 #pragma unroll
   for (int j = 0; j < kTpt; ++j)
     if (j < tpt && tid + j * NT < tiles) mu_l = fmaxf(mu_l, ms_max(mst[j]));
-  uint32_t gmx = mu_l == -INFINITY ? 0u : ord_from_f32(mu_l);
-#pragma unroll
-  for (int x = 1; x < GS; x <<= 1) gmx = max(gmx, (uint32_t)__shfl_xor((int)gmx, x));
-  // Group maxima as distinct keys (max, then 64 - group): the key of rank
-  // k - 1 holds the k-th largest maximum counted with multiplicity.
-  if ((lane & (GS - 1)) == 0)
-    sh.sc[0][tid / GS] = ((uint64_t)gmx << 32) | (uint32_t)(kWave - tid / GS);
+  // Tile t belongs to group t mod 64, the lane of the thread that holds it:
+  // every group has a tile once there are 64, and up to 64 tiles each tile
+  // is a group of its own, so whenever there are k tiles the k-th largest
+  // group maximum is a logit that bounds the row's k-th largest from below.
+  // (Groups of consecutive threads instead left most groups empty on small
+  // heads or with large k, and the bound fell to zero.)
+  sh.gm[wave][lane] = mu_l == -INFINITY ? 0u : ord_from_f32(mu_l);
   const float mw = wave_max(mu_l);
   if (lane == 0) sh.f[wave] = mw;
   if (tid == 0) {
@@ -846,15 +846,20 @@ __device__ void row_merge(const HeadArgs &a, int m, MergeShared<WAVES> &sh, int3
     if (j < tpt && tid + j * NT < tiles) s_l += ms_sum(mst[j]) * __expf(ms_max(mst[j]) - mu);
   const float sw = wave_sum(s_l);
   if (lane == 0) sh.f2[wave] = sw;
-  // Rank of each group key: every wave counts the larger keys among its
-  // 64 / WAVES of them (broadcast reads); after the barrier every wave sums
-  // the partial counts and takes the key of rank k - 1.
+  // Group maxima as distinct keys (max, then 64 - group): the key of rank
+  // k - 1 holds the k-th largest maximum counted with multiplicity. Every
+  // wave forms all 64 keys (lane = group); each counts the larger keys among
+  // 64 / WAVES of them; after the barrier every wave sums the partial
+  // counts and takes the key of rank k - 1.
+  uint32_t gmx = 0;
+#pragma unroll
+  for (int w = 0; w < WAVES; ++w) gmx = max(gmx, sh.gm[w][lane]);
+  const uint64_t gkey = ((uint64_t)gmx << 32) | (uint32_t)(kWave - lane);
   constexpr int kSpan = kWave / WAVES;
   static_assert(kSpan * WAVES == kWave && WAVES <= 16, "group keys split evenly over the waves");
-  const uint64_t gkey = sh.sc[0][lane];
   uint32_t c = 0;
 #pragma unroll
-  for (int j = 0; j < kSpan; ++j) c += sh.sc[0][wave * kSpan + j] > gkey;
+  for (int j = 0; j < kSpan; ++j) c += readlane_u64(gkey, wave * kSpan + j) > gkey;
   uint32_t *prank = &sh.prank[0][0][0];
   prank[wave * kWave + lane] = c;
   __syncthreads();
