@@ -213,7 +213,7 @@ __device__ __forceinline__ void quad_draw_publish(const HeadArgs &a, int m0, int
 
 constexpr int kMaxTiles = VT_VHIGH_MAX / kTileRows;
 
-constexpr int kCandCap = 1024;   // survivors the final merge can hold
+constexpr int kCandCap = 4096;   // survivors the final merge can hold (every logit of 64 tiles)
 
 template <int WAVES>
 struct alignas(16) MergeShared {
