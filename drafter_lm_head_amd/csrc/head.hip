@@ -1370,11 +1370,11 @@ constexpr int kRingMinPairs = 256;
 
 // Both operands are copied from memory straight into LDS (buffer loads with
 // the LDS flag: each lane's 16 bytes land in slot lane of a 64-slot block, no
-// registers involved), through a ring of S stages, so that S - 1 K steps are
-// in flight per workgroup at no register cost. A stage holds the 128 W rows,
-// then the draft rows, 8 chunks each in the swizzled order of gemm_slot; lane
-// l of a load fills row l / 8 of its 8-row block at position l % 8, so it
-// reads chunk (l % 8) ^ (l / 8) of that row. Chunks past d and rows past
+// registers involved), through a ring of S stages, so that up to S - 1 K
+// steps are in flight per workgroup at no register cost. A stage holds the
+// W rows, then the draft rows, 8 chunks each in the swizzled order of
+// gemm_slot; lane l of a load fills row l / 8 of its 8-row block at position
+// l % 8, so it reads chunk (l % 8) ^ (l / 8) of that row. Chunks past d and rows past
 // V_high or M are addressed outside the buffer ranges, which the hardware
 // turns into zeros in LDS.
 template <int CB, int S, int TPW>
@@ -1506,7 +1506,12 @@ __global__ __launch_bounds__(4 * TPW * kWave) void head_gemm_kernel(HeadArgs a) 
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    issue(s + S - 1);
+    // With two stages the next step's loads go out at once, since they must
+    // land within this step; with more they go out behind this step's LDS
+    // reads, which they would otherwise hold up (4096 x 32768 head, M = 160 /
+    // 192 / 256: 77.3 / 79.0 / 83.9 -> 72.6 / 75.3 / 79.1 us; with four
+    // stages, up to 128 rows, no change).
+    if constexpr (S == 2) issue(s + S - 1);
     const u32x4 *st = ring + (s % S) * kSlots;
 #pragma unroll
     for (int t = 0; t < kGemmKC / 4; ++t) {
@@ -1524,6 +1529,7 @@ __global__ __launch_bounds__(4 * TPW * kWave) void head_gemm_kernel(HeadArgs a) 
               0, 0, 0);
       }
     }
+    if constexpr (S > 2) issue(s + S - 1);
   }
   // No load into this workgroup's LDS may outlive it.
   wait_vmcnt<0>();
