@@ -1451,10 +1451,11 @@ __global__ __launch_bounds__(4 * TPW * kWave) void head_gemm_kernel(HeadArgs a) 
   // to 32 rows and 0.5 to 4 us slower from 60 rows on.
   const int steps = (c16 + kGemmKC - 1) / kGemmKC;
   const int rot = ((a.M <= 32 ? 3 : 1) * (p / 8)) % steps;
-  // K step s (the workgroup's s-th, step se of d) into ring stage s % S;
-  // every step is issued, steps past the last (and chunks past d) as
-  // out-of-range zero loads.
-  auto issue = [&](int s) {
+  // K step s (the workgroup's s-th, step se of d) into ring stage s % S:
+  // its W loads (part 1), its draft-row loads (part 2) or both; every step
+  // is issued, steps past the last (and chunks past d) as out-of-range zero
+  // loads.
+  auto issue = [&](int s, int part) {
     const int se = s < steps ? (s + rot < steps ? s + rot : s + rot - steps) : s;
     // All ones past d, else zero (arithmetic, so that no lane branches).
     const uint32_t past = ~(uint32_t)((se * kGemmKC + lchunk - c16) >> 31);
@@ -1463,10 +1464,12 @@ __global__ __launch_bounds__(4 * TPW * kWave) void head_gemm_kernel(HeadArgs a) 
     for (int j = 0; j < kLoads; ++j) {
       const uint32_t off = (voff[j] + (uint32_t)se * (kGemmKC * 16)) | (past & 0x7fffff00u);
       auto *dst = (__attribute__((address_space(3))) void *)(stage + 64 * (wave + kWaves * j));
-      if (j < kWLoads)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, dst, 16, off, 0, 0, kShared ? 0 : kCpolNt);
-      else
+      if (j < kWLoads) {
+        if (part & 1)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, dst, 16, off, 0, 0, kShared ? 0 : kCpolNt);
+      } else if (part & 2) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(hres, dst, 16, off, 0, 0, 0);
+      }
     }
   };
   const int wr = TPW == 2 ? wave & 1 : 0, wc = TPW == 2 ? wave >> 1 : wave;
@@ -1478,7 +1481,7 @@ __global__ __launch_bounds__(4 * TPW * kWave) void head_gemm_kernel(HeadArgs a) 
     for (int cb = 0; cb < CB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s) issue(s);
+  for (int s = 0; s < S - 1; ++s) issue(s, 3);
   EarlyDraw<CB> early;
   if constexpr (kEarlyDraw<CB>) {
     if (a.sample) {
@@ -1506,12 +1509,16 @@ __global__ __launch_bounds__(4 * TPW * kWave) void head_gemm_kernel(HeadArgs a) 
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    // With two stages the next step's loads go out at once, since they must
-    // land within this step; with more they go out behind this step's LDS
-    // reads, which they would otherwise hold up (4096 x 32768 head, M = 160 /
-    // 192 / 256: 77.3 / 79.0 / 83.9 -> 72.6 / 75.3 / 79.1 us; with four
-    // stages, up to 128 rows, no change).
-    if constexpr (S == 2) issue(s + S - 1);
+    // With three stages or more the next step's loads go out after this
+    // step's MFMAs, behind its LDS reads, which they would otherwise hold up
+    // (4096 x 32768 head, M = 160 / 192 / 256: 77.3 / 79.0 / 83.9 -> 72.6 /
+    // 75.3 / 79.1 us; with four stages, up to 128 rows, no change). With two
+    // they must land within this step: the W loads, from HBM, go out at
+    // once, and the draft-row loads, which hit in L2 and are most of the
+    // bytes, halfway through the step (M = 320 / 384 / 512: 110.0 / 113.7 /
+    // 143.6 us all at once, 98.9 / 104.6 / 128.5 so; a quarter of the way
+    // 103.6 / 109.2 / 136.1, after the MFMAs 110.3 / 114.1 / 141.9).
+    if constexpr (S == 2) issue(s + 1, 1);
     const u32x4 *st = ring + (s % S) * kSlots;
 #pragma unroll
     for (int t = 0; t < kGemmKC / 4; ++t) {
@@ -1528,8 +1535,9 @@ __global__ __launch_bounds__(4 * TPW * kWave) void head_gemm_kernel(HeadArgs a) 
               __builtin_bit_cast(bf16x8, av[rb]), __builtin_bit_cast(bf16x8, bv), acc[rb][cb],
               0, 0, 0);
       }
+      if constexpr (S == 2) if (t == 0) issue(s + 1, 2);
     }
-    if constexpr (S > 2) issue(s + S - 1);
+    if constexpr (S > 2) issue(s + S - 1, 3);
   }
   // No load into this workgroup's LDS may outlive it.
   wait_vmcnt<0>();
