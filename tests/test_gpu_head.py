@@ -75,12 +75,17 @@ def test_draft_tree_rows(dlh, M):
                                            (8193, 128, 64, 60), (12288, 64, 33, 60),
                                            (4097, 520, 33, 130), (65, 8, 64, 193),
                                            (777, 8192, 10, 64), (300, 8192, 16, 200),
-                                           (300, 8, 8, 40), (200, 8192, 10, 512)])
+                                           (300, 8, 8, 40), (200, 8192, 10, 512),
+                                           (4097, 520, 10, 300), (1000, 72, 10, 400),
+                                           (65, 8, 64, 385)])
 def test_draft_tree_edges(dlh, V_high, d, k, M):
     # Ragged tiles and row groups: a last tile of one row, a last group of
     # two (M = 130) or one (M = 193) draft rows; the longest rows (d = 8192)
     # on the GEMM tiling's single-tile and tile-pair workgroups, and one
-    # 16-byte chunk per row (d = 8).
+    # 16-byte chunk per row (d = 8). Past 256 rows (two ring stages, the
+    # draft-row loads issued halfway through each step) an odd number of K
+    # steps with a partial last one (d = 520), a single partial step (72)
+    # and a single chunk (8).
     h, W, t2f = rand_case(300 + V_high, M, d, V_high, hscale=2.0)
     check_case(dlh, h, W, t2f, min(k, V_high))
 

@@ -58,6 +58,17 @@ def test_draws_match_oracle_gemv_and_mfma(dlh, M):
         assert check_draws(ids, probs, h, W, t2f, 0xDEADBEEF12345, off) <= max(1, M // 64)
 
 
+@pytest.mark.parametrize("M,d,V_high", [(300, 520, 4097), (384, 72, 1000)])
+def test_two_stage_draws_with_ragged_hidden_size(dlh, M, d, V_high):
+    # Draws on the 96-row blocks (two ring stages, draft-row loads halfway
+    # through each K step) with a partial last K step and an odd number of
+    # steps (d = 520), or one partial step (d = 72).
+    h, W, t2f = rand_case(700 + M, M, d, V_high, hscale=4.0)
+    for off in (0, 3):
+        ids, probs = draw(dlh, h, W, t2f, 0x5EED, off)
+        assert check_draws(ids, probs, h, W, t2f, 0x5EED, off) <= max(1, M // 64)
+
+
 @pytest.mark.parametrize("V_high", [1, 64, 65, 200, 40000])
 def test_two_row_draws_few_and_many_workgroups(dlh, V_high):
     # Two rows: one merging workgroup (one tile) or two in parallel; the
