@@ -50,8 +50,8 @@ def test_tiny_pipeline_draws_match_oracle(dlh):
 
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 16, 33, 60, 64, 65, 130, 300, 384, 385, 512])
 def test_draws_match_oracle_gemv_and_mfma(dlh, M):
-    # Past 256 rows the draw runs on 96-row blocks up to 384 rows, on two
-    # groups of 256 rows beyond.
+    # Past 256 rows the draw runs on 80- and 96-row blocks up to 384 rows,
+    # on two groups of 256 rows beyond.
     h, W, t2f = rand_case(100 + M, M, 512, 3000, hscale=6.0)   # ragged V_high
     for off in (0, 1, 2**40 + 5):
         ids, probs = draw(dlh, h, W, t2f, 0xDEADBEEF12345, off)
@@ -60,9 +60,9 @@ def test_draws_match_oracle_gemv_and_mfma(dlh, M):
 
 @pytest.mark.parametrize("M,d,V_high", [(300, 520, 4097), (384, 72, 1000)])
 def test_two_stage_draws_with_ragged_hidden_size(dlh, M, d, V_high):
-    # Draws on the 96-row blocks (two ring stages, draft-row loads halfway
-    # through each K step) with a partial last K step and an odd number of
-    # steps (d = 520), or one partial step (d = 72).
+    # Draws on the 80- and 96-row blocks (two ring stages, draft-row loads
+    # halfway through each K step) with a partial last K step and an odd
+    # number of steps (d = 520), or one partial step (d = 72).
     h, W, t2f = rand_case(700 + M, M, d, V_high, hscale=4.0)
     for off in (0, 3):
         ids, probs = draw(dlh, h, W, t2f, 0x5EED, off)
