@@ -1515,9 +1515,10 @@ __global__ __launch_bounds__(4 * TPW * kWave) void head_gemm_kernel(HeadArgs a) 
     // 75.3 / 79.1 us; with four stages, up to 128 rows, no change). With two
     // they must land within this step: the W loads, from HBM, go out at
     // once, and the draft-row loads, which hit in L2 and are most of the
-    // bytes, halfway through the step (M = 320 / 384 / 512: 110.0 / 113.7 /
-    // 143.6 us all at once, 98.9 / 104.6 / 128.5 so; a quarter of the way
-    // 103.6 / 109.2 / 136.1, after the MFMAs 110.3 / 114.1 / 141.9).
+    // bytes, halfway through the step (M = 320 / 384 on 6 blocks per wave
+    // and 512 on 8: 110.0 / 113.7 / 143.6 us all at once, 98.9 / 104.6 /
+    // 128.5 so; a quarter of the way 103.6 / 109.2 / 136.1, after the MFMAs
+    // 110.3 / 114.1 / 141.9).
     if constexpr (S == 2) issue(s + 1, 1);
     const u32x4 *st = ring + (s % S) * kSlots;
 #pragma unroll
