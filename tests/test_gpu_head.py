@@ -61,12 +61,14 @@ def test_draft_rows(dlh, M):
     check_case(dlh, h, W, t2f, 10)
 
 
-@pytest.mark.parametrize("M", [17, 33, 60, 64, 65, 100, 128, 192, 257, 320, 448, 512])
+@pytest.mark.parametrize("M", [17, 33, 60, 64, 65, 100, 128, 192, 257, 320, 321, 448, 449,
+                               512])
 def test_draft_tree_rows(dlh, M):
     # On this small head (too few tile pairs for the GEMM tiling) up to 32
     # rows run the 64-row MFMA kernel, past 32 the GEMM tiling (one more
     # 16-row block per wave for every 64 rows: full blocks at 64, 128, 192,
-    # 320, 448, 512); then one merge workgroup per row.
+    # 320, 448, 512, one row past them at 257, 321, 449); then one merge
+    # workgroup per row.
     h, W, t2f = rand_case(200 + M, M, 1024, 2500)
     check_case(dlh, h, W, t2f, 10)
 
