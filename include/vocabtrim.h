@@ -199,7 +199,8 @@ int vt_gather_bias(const uint16_t *b, int32_t V, const int32_t *t2f, int32_t V_h
  *               partial and the tile's top-k keys; the last workgroups to
  *               finish merge them. No logit is written to memory.
  *   otherwise   a GEMM-tiled MFMA kernel (one workgroup per 128 kept rows,
- *               or per 64 when V_high <= 32640, over every draft row, both
+ *               or per 64 up to 64 draft rows when V_high <= 32640 and up
+ *               to 128 when V_high <= 16384, over every draft row, both
  *               operands copied into an LDS ring), then one merge workgroup
  *               per draft row. The fp32 logits of every tile of 64 kept rows
  *               go to the workspace and the merge reads back those of the
