@@ -15,7 +15,7 @@ bytes of one call by the average call time over the timed region, taken
 with HIP events on the stream the kernel runs on.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--M M] [--sweep] [--no-cpu] [--only-head] [--calib-copy]
+                       [--M M] [--sweep] [--no-cpu] [--only-head [--sample]] [--calib-copy]
 """
 from __future__ import annotations
 
@@ -192,6 +192,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only-head", action="store_true",
                     help="time only the cold draft-head steps (for profiler runs)")
+    ap.add_argument("--sample", action="store_true",
+                    help="with --only-head: time vt_draft_sample (one draw per row) instead")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -254,6 +256,19 @@ def main():
     def warm(i):
         dlh.vt_draft_head(h, Wt, t2f, k, full_ids=full_ids, probs=probs, ws=ws)
 
+    kk = k
+    if args.only_head and args.sample:
+        # The draw instead of top-k (same contraction, per-tile Gumbel-max
+        # draws, one output per row), a new offset per call.
+        kk = 1
+        s_ws = torch.zeros(dlh.vt_draft_head_workspace_size(M, V_high, d, 1), dtype=torch.uint8,
+                           device=dev)
+        s_out = (torch.empty(M, dtype=torch.int32, device=dev),
+                 torch.empty(M, dtype=torch.float32, device=dev))
+
+        def cold(i):
+            dlh.vt_draft_sample(h, copies[i % R], t2f, 2024, i, full_ids=s_out[0],
+                                probs=s_out[1], ws=s_ws)
     for i in range(args.warmup):
         cold(i)
     torch.cuda.synchronize()
@@ -261,7 +276,7 @@ def main():
     ms_total = time_calls(cold, args.steps, torch)
     ms_step = ms_total / args.steps
     value = 1000.0 / ms_step
-    nb = head_bytes(V_high, d, M, k)
+    nb = head_bytes(V_high, d, M, kk)
     # Roofline: algorithmic bytes over the kernel's average duration in the
     # timed region (events on the stream the kernel runs on).
     achieved = nb / (ms_step * 1e-3) / 1e9
@@ -277,7 +292,8 @@ def main():
     if args.only_head:
         print(json.dumps({"metric": METRIC, "value": round(value, 1), "unit": "calls/s",
                           "ms_per_step": round(ms_step, 6), "steps": args.steps,
-                          "GB_per_s": round(achieved, 1)}), flush=True)
+                          "GB_per_s": round(achieved, 1), "draw": bool(args.sample)}),
+              flush=True)
         return
     n_launch = min(args.steps, 1000)
     us_launch = per_launch_us(cold, n_launch, torch)
