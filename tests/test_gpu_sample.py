@@ -69,6 +69,18 @@ def test_two_stage_draws_with_ragged_hidden_size(dlh, M, d, V_high):
         assert check_draws(ids, probs, h, W, t2f, 0x5EED, off) <= max(1, M // 64)
 
 
+@pytest.mark.parametrize("M,d,V_high", [(150, 72, 1000), (200, 520, 4097), (256, 4096, 700),
+                                         (450, 8, 700)])
+def test_draws_on_3_and_4_blocks_with_few_k_steps(dlh, M, d, V_high):
+    # Draws on 3 and 4 blocks per wave (and past 384 rows on two groups of
+    # 256) with hidden sizes of 2 K steps (d = 72), 9 (520), 1 (8) and 64
+    # (4096): the variates drawn in the epilogue whatever the step count.
+    h, W, t2f = rand_case(800 + M, M, d, V_high, hscale=4.0)
+    for off in (0, 5):
+        ids, probs = draw(dlh, h, W, t2f, 0xC0FFEE, off)
+        assert check_draws(ids, probs, h, W, t2f, 0xC0FFEE, off) <= max(1, M // 64)
+
+
 @pytest.mark.parametrize("V_high", [1, 64, 65, 200, 40000])
 def test_two_row_draws_few_and_many_workgroups(dlh, V_high):
     # Two rows: one merging workgroup (one tile) or two in parallel; the
