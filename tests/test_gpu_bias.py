@@ -52,9 +52,10 @@ def test_gather_bias_copies_kept_entries_and_counts_bad_ones(dlh):
     assert oracle.gather(b[:, None], t2f[good])[:, 0].tobytes() == got[good].tobytes()
 
 
-@pytest.mark.parametrize("M", [1, 3, 4, 5, 20, 60, 130])
+@pytest.mark.parametrize("M", [1, 3, 4, 5, 20, 60, 130, 192, 300, 448])
 def test_biased_head_matches_oracle(dlh, M):
-    # GEMV path up to 2 rows, the MFMA path beyond; V_high is ragged.
+    # GEMV path up to 2 rows, the MFMA path beyond (past 128 rows the GEMM
+    # tiling's 3-, 5- and 7-block shapes); V_high is ragged.
     h, W, b, t2f = biased_case(100 + M, M, 512, 3001)
     k = 10
     ids, probs = dlh.vt_draft_head_bias(to_dev_bf16(h), to_dev_bf16(W), to_dev_bf16(b),
@@ -100,11 +101,13 @@ def test_biased_head_full_size(dlh, M):
     check_picks(ids.cpu().numpy(), probs.cpu().numpy(), z_o, t2f, w.k, ids_o)
 
 
-@pytest.mark.parametrize("M,V_high", [(2, 2000), (9, 2000), (70, 2000), (2, 33000), (40, 33000)])
+@pytest.mark.parametrize("M,V_high", [(2, 2000), (9, 2000), (70, 2000), (2, 33000), (40, 33000),
+                                      (180, 2000), (300, 2000)])
 def test_biased_draws_match_oracle(dlh, M, V_high):
-    # Small heads: GEMV (two rows), 64-row kernel, GEMM tiling; heads of 256 or
-    # more tile pairs: the GEMM tiling with its variates drawn before the K
-    # loop, here with a ragged last tile pair.
+    # Small heads: GEMV (two rows), 64-row kernel, GEMM tiling (3 and 5
+    # blocks per wave past 128 rows); heads of 256 or more tile pairs: the
+    # GEMM tiling with its variates drawn before the K loop, here with a
+    # ragged last tile pair.
     h, W, b, t2f = biased_case(300 + M, M, 256, V_high, bias_std=2.0)
     near = 0
     for off in range(4):
